@@ -1,0 +1,243 @@
+"""Benchmark of the TurboQuant decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: quantize-append one new
+token per sequence into the paged pool, then fused decode attention over
+every sequence's full context. Inputs are seeded synthetic data already
+resident in HBM (see workloads/). Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload k8v4]
+
+Timing: K steps back to back on one stream, bracketed by synchronisation,
+with HIP events around every quantize and decode launch. The decode call
+runs a split kernel and a reduce kernel; its event-timed duration is the
+"dominant kernel" time of the roofline object. Pools too small to defeat the
+256 MB Infinity Cache are replicated and rotated (step i reads pool i mod n).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 << 20         # Infinity Cache
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_pmc.json")
+
+
+def _sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_source_sha():
+    c = os.path.join(ROOT, "compressed_decode_attention_quantize_amd", "csrc")
+    return _sha([os.path.join(c, "tq_decode.hip"), os.path.join(c, "tq_device.h")])
+
+
+def _traffic(workload_name, per_launch_bytes):
+    """HBM bytes per decode launch from committed PMC counters, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(PMC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload_name)
+    if not entry or entry.get("source_sha") != kernel_source_sha():
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(built, budget_s: float):
+    """The oracle's decode attention timed on host cores over a bounded
+    sample (whole sequences of the same workload, oracle-encoded from the same
+    K/V), in KV tokens per second."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as OA
+    from oracle import codec as OX
+    from oracle import config as OC
+
+    w = built.w
+    cfg = built.cfg
+    ocfg = OC.TQConfig(head_dim=cfg.head_dim, key_quant_bits=cfg.key_quant_bits,
+                       value_quant_bits=cfg.value_quant_bits, seed=int(cfg.seed),
+                       norm_correction=bool(cfg.norm_correction))
+    b = min(built.captured)
+    k, v = built.captured[b]
+    n = k.shape[0]
+    bs = w.block_size
+    nblk = max(1, -(-n // bs))
+    pool = np.zeros((nblk, w.num_kv_heads, bs, ocfg.slot_size_aligned), np.uint8)
+    for s0 in range(0, n, 16384):
+        OX.append(pool, k[s0:s0 + 16384], v[s0:s0 + 16384], np.arange(s0, min(n, s0 + 16384)), ocfg, 0)
+    q = built.q[b:b + 1].float().cpu().numpy()
+    table = np.arange(nblk, dtype=np.int32)[None]
+    ring = {}
+    if w.ring:
+        ring = dict(ring_k=built.ring_k[b:b + 1].float().cpu().numpy(),
+                    ring_v=built.ring_v[b:b + 1].float().cpu().numpy(),
+                    ring_lens=np.array([w.ring]))
+    tokens = 0
+    reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            OA.decode_attention(q, pool, table, [n], ocfg, 0, **ring)
+            tokens += n + w.ring
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    return {"value": tokens / el, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequence {b} ({n} compressed + {w.ring} ring tokens, {w.num_q_heads} q heads) "
+                      f"decoded {reps}x in {el:.1f} s, numpy single-threaded"}
+
+
+def bulk_quantize(built, tq, torch, chunk=65536, reps=5):
+    """Quantize-append throughput: `chunk`-token appends into pool 0 (rewriting
+    sequence 0's leading positions), events around each call."""
+    from workloads import KVSource, slot_ids_for
+    w = built.w
+    n = min(chunk, int(built.lens_np[0]))
+    src = KVSource(w, "cuda", stream_id=77)
+    k, v = src.kv(n)
+    ids = torch.from_numpy(slot_ids_for(built.tables_np, 0, 0, n, w.block_size)).cuda()
+    call = tq.prepare_quantize(built.cfg, 0, k, v, ids, built.pools[0])
+    for _ in range(2):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    return n, ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="k8v4")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import compressed_decode_attention_quantize_amd as tq
+    from workloads import WORKLOADS
+    from workloads import gpu as WG
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    cfg = tq.config_from_preset(w.preset, w.head_dim) if w.preset else tq.config_init(w.head_dim, w.key_bits, w.value_bits)
+    from workloads import sequence_lengths
+    pool_bytes = int(sequence_lengths(w).sum()) * w.num_kv_heads * cfg.slot_size_aligned
+    n_pools = 1 if pool_bytes > 2 * MALL_BYTES else max(1, -(-3 * MALL_BYTES // max(pool_bytes, 1)))
+    n_pools = min(n_pools, 8)
+    print(f"[bench] building {w.name}: {w.description}; {n_pools} pool(s) of {pool_bytes / 1e6:.1f} MB",
+          file=sys.stderr, flush=True)
+    built = WG.build(w, "cuda", n_pools=n_pools, capture=(0,))
+    steps = WG.prepare_steps(built, args.split_tokens)
+    _, nsplit = tq.decode_workspace_size(cfg, w.batch, w.num_q_heads, built.max_seq_len, w.ring, args.split_tokens)
+
+    for i in range(args.warmup):
+        qc, dc = steps[i % n_pools]
+        qc()
+        dc()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        qc, dc = steps[i % n_pools]
+        ev[i][0].record()
+        qc()
+        ev[i][1].record()
+        dc()
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    qnt_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+    kv_tokens = int(built.lens_np.sum()) + w.batch * w.ring
+    value = kv_tokens / (ms_step / 1e3)
+    dbytes = WG.decode_bytes(built)
+    dec_mean = float(dec_ms.mean())
+    achieved = dbytes / (dec_mean / 1e3) / 1e9
+    traffic = _traffic(w.name, dbytes)
+
+    nq, qms = bulk_quantize(built, tq, torch)
+    qbpt = WG.quantize_bytes_per_token(built)
+
+    result = {
+        "metric": "decode-attn KV tokens/s + achieved HBM GB/s (% peak); quantize tokens/s",
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "preset": w.preset,
+                   "head_dim": w.head_dim, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "batch": w.batch, "context": w.context, "ring": w.ring, "block_size": w.block_size,
+                   "kv_tokens_per_step": kv_tokens, "splits_per_seq": nsplit, "pools_rotated": n_pools,
+                   "parallelism": "single GPU"},
+        "decode": {"ms_mean": dec_mean, "ms_p10": float(np.percentile(dec_ms, 10)),
+                   "ms_p50": float(np.median(dec_ms)), "ms_p90": float(np.percentile(dec_ms, 90)),
+                   "algorithmic_bytes": dbytes, "GBps": achieved, "pct_hbm_peak": 100 * achieved / HBM_PEAK_GBS,
+                   "kv_tokens_per_s": kv_tokens / (dec_mean / 1e3)},
+        "quantize_step": {"ms_mean": float(qnt_ms.mean()), "tokens": w.batch},
+        "quantize_bulk": {"tokens": nq, "ms": qms, "tokens_per_s": nq / (qms / 1e3),
+                          "GBps": nq * qbpt / (qms / 1e3) / 1e9, "bytes_per_token": qbpt},
+        "roofline": {"bound": "hbm", "kernel": "tq_decode_attention (split + reduce kernels)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "wall_s_timed": wall,
+        "library": tq.version(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(built, args.cpu_budget)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,360 @@
+"""Python binding of libtq (the MI355X TurboQuant KV-cache library).
+
+Argument marshalling only: every step of quantize, decode and dequant runs in
+the library's HIP kernels. torch tensors supply device memory and the current
+stream. Importing this module loads ``libtq.so`` from this directory and
+raises ``ImportError`` when it is missing (build it with
+``python compressed_decode_attention_quantize_amd/csrc/build.py``); there is
+no fallback path.
+
+The functions mirror include/tq.h:
+
+* ``config_from_preset(name, head_dim)`` / ``config_init(...)`` -> ``Config``
+* ``slot_size(cfg, aligned=True)``, ``page_size(cfg, num_kv_heads, block_size)``
+* ``layer_signs(cfg, layer_idx)``
+* ``quantize_append(cfg, layer_idx, k, v, slot_mapping, kv_pool)``
+* ``decode_workspace_size(cfg, batch, num_q_heads, max_seq_len, ring_cap, split_tokens)``
+* ``decode_attention(cfg, layer_idx, q, kv_pool, block_tables, seq_lens, max_seq_len, ...)``
+* ``dequant(cfg, layer_idx, kv_pool, slot_ids)``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libtq.so not found at {LIB_PATH}; build it with "
+        "`python compressed_decode_attention_quantize_amd/csrc/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+TQ_OK = 0
+STATUS_NAMES = {0: "TQ_OK", 1: "TQ_ERR_INVALID_ARG", 2: "TQ_ERR_UNKNOWN_PRESET",
+                3: "TQ_ERR_UNSUPPORTED", 4: "TQ_ERR_WORKSPACE", 5: "TQ_ERR_HIP"}
+F32, BF16, F16 = 0, 1, 2
+
+EXPORTED = ["tq_config_init", "tq_config_from_preset", "tq_slot_size", "tq_page_size",
+            "tq_layer_signs", "tq_quantize_append", "tq_decode_workspace_size",
+            "tq_decode_attention", "tq_dequant", "tq_last_error", "tq_version"]
+
+
+class Config(ctypes.Structure):
+    """Mirror of tq_config (include/tq.h)."""
+    _fields_ = [
+        ("head_dim", ctypes.c_int32), ("key_quant_bits", ctypes.c_int32),
+        ("value_quant_bits", ctypes.c_int32), ("norm_correction", ctypes.c_int32),
+        ("seed", ctypes.c_int64),
+        ("key_fp8", ctypes.c_int32), ("mse_bits", ctypes.c_int32),
+        ("key_mse_bits", ctypes.c_int32), ("centroid_bits", ctypes.c_int32),
+        ("n_centroids", ctypes.c_int32), ("key_packed_size", ctypes.c_int32),
+        ("value_packed_size", ctypes.c_int32), ("slot_size", ctypes.c_int32),
+        ("slot_size_aligned", ctypes.c_int32), ("wht_block", ctypes.c_int32),
+        ("centroids", ctypes.c_float * 16), ("midpoints", ctypes.c_float * 15),
+    ]
+
+    def __repr__(self):
+        return (f"Config(head_dim={self.head_dim}, key_quant_bits={self.key_quant_bits}, "
+                f"value_quant_bits={self.value_quant_bits}, norm_correction={bool(self.norm_correction)}, "
+                f"seed={self.seed}, slot_size_aligned={self.slot_size_aligned})")
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_P = ctypes.c_void_p
+_i32, _i64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_CP = ctypes.POINTER(Config)
+
+_lib.tq_config_init.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _CP]
+_lib.tq_config_from_preset.argtypes = [ctypes.c_char_p, ctypes.c_int, _CP]
+_lib.tq_slot_size.argtypes = [_CP, ctypes.c_int]
+_lib.tq_slot_size.restype = _i32
+_lib.tq_page_size.argtypes = [_CP, ctypes.c_int, ctypes.c_int]
+_lib.tq_page_size.restype = _i64
+_lib.tq_layer_signs.argtypes = [_CP, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+_lib.tq_quantize_append.argtypes = [_CP, ctypes.c_int, _P, _P, ctypes.c_int, _i64, ctypes.c_int,
+                                    _i64, _i64, _P, _P, _i64, ctypes.c_int, _P]
+_lib.tq_decode_workspace_size.argtypes = [_CP, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.POINTER(_sz), ctypes.POINTER(ctypes.c_int)]
+_lib.tq_decode_attention.argtypes = [_CP, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, _P, _i64, ctypes.c_int, _P, ctypes.c_int, _P,
+                                     ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _sz,
+                                     ctypes.c_int, _P]
+_lib.tq_dequant.argtypes = [_CP, ctypes.c_int, _P, _i64, ctypes.c_int, ctypes.c_int, _P, _i64, _P, _P, _P]
+for _name in ("tq_config_init", "tq_config_from_preset", "tq_layer_signs", "tq_quantize_append",
+              "tq_decode_workspace_size", "tq_decode_attention", "tq_dequant"):
+    getattr(_lib, _name).restype = ctypes.c_int
+_lib.tq_last_error.restype = ctypes.c_char_p
+_lib.tq_version.restype = ctypes.c_char_p
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def last_error() -> str:
+    return _lib.tq_last_error().decode()
+
+
+def version() -> str:
+    return _lib.tq_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != TQ_OK:
+        raise TQError(status, last_error())
+
+
+# ----------------------------------------------------------------------------- config
+
+def config_init(head_dim: int, key_bits: int, value_bits: int, norm_correction: bool = False,
+                seed: int = 42) -> Config:
+    c = Config()
+    _check(_lib.tq_config_init(head_dim, key_bits, value_bits, int(bool(norm_correction)), seed,
+                               ctypes.byref(c)))
+    return c
+
+
+def config_from_preset(preset: str, head_dim: int) -> Config:
+    c = Config()
+    _check(_lib.tq_config_from_preset(preset.encode(), head_dim, ctypes.byref(c)))
+    return c
+
+
+def slot_size(cfg: Config, aligned: bool = True) -> int:
+    n = _lib.tq_slot_size(ctypes.byref(cfg), int(aligned))
+    if n < 0:
+        raise TQError(1, last_error())
+    return n
+
+
+def page_size(cfg: Config, num_kv_heads: int, block_size: int) -> int:
+    n = _lib.tq_page_size(ctypes.byref(cfg), num_kv_heads, block_size)
+    if n < 0:
+        raise TQError(1, last_error())
+    return n
+
+
+def layer_signs(cfg: Config, layer_idx: int):
+    import numpy as np
+    out = (ctypes.c_float * cfg.head_dim)()
+    _check(_lib.tq_layer_signs(ctypes.byref(cfg), layer_idx, out))
+    return np.frombuffer(out, dtype=np.float32).copy()
+
+
+# ----------------------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float16:
+        return F16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, float16)")
+
+
+def _dev(t, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream_ptr(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def quantize_append(cfg: Config, layer_idx: int, k, v, slot_mapping, kv_pool, stream=None) -> None:
+    """k, v: [T, Hkv, D] (or [T, Hkv*D] rows with a token stride) float32/bf16/f16
+    with the head and element dims contiguous; slot_mapping int64 [T];
+    kv_pool uint8 [num_blocks, Hkv, block_size, S]."""
+    torch = _torch()
+    _dev(k, "k")
+    _dev(v, "v")
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(kv_pool, "kv_pool", torch.uint8)
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must have the same dtype")
+    if kv_pool.dim() != 4 or kv_pool.shape[3] != cfg.slot_size_aligned or not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be contiguous [num_blocks, Hkv, block_size, slot_size_aligned]")
+    t_count = k.shape[0]
+    hkv = kv_pool.shape[1]
+    for name, x in (("k", k), ("v", v)):
+        if x.dim() != 3 or x.shape[1] != hkv or x.shape[2] != cfg.head_dim:
+            raise ValueError(f"{name} must be [T, {hkv}, {cfg.head_dim}]")
+        if x.stride(2) != 1 or x.stride(1) != cfg.head_dim:
+            raise ValueError(f"{name}: heads and elements must be contiguous")
+    if v.shape[0] != t_count or slot_mapping.shape != (t_count,) or not slot_mapping.is_contiguous():
+        raise ValueError("k, v and slot_mapping disagree on the token count")
+    s = stream if stream is not None else _stream_ptr(k)
+    _check(_lib.tq_quantize_append(ctypes.byref(cfg), layer_idx, k.data_ptr(), v.data_ptr(), _dtype_code(k),
+                                   t_count, hkv, k.stride(0) if t_count > 1 else hkv * cfg.head_dim,
+                                   v.stride(0) if t_count > 1 else hkv * cfg.head_dim,
+                                   slot_mapping.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
+                                   kv_pool.shape[2], s))
+
+
+def decode_workspace_size(cfg: Config, batch: int, num_q_heads: int, max_seq_len: int,
+                          ring_cap: int = 0, split_tokens: int = 0):
+    """Returns (bytes, chunks per sequence)."""
+    b = _sz()
+    n = ctypes.c_int()
+    _check(_lib.tq_decode_workspace_size(ctypes.byref(cfg), batch, num_q_heads, max_seq_len, ring_cap,
+                                         split_tokens, ctypes.byref(b), ctypes.byref(n)))
+    return b.value, n.value
+
+
+def decode_attention(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_lens, max_seq_len: int,
+                     ring_k=None, ring_v=None, ring_lens=None, softmax_scale: float = 0.0,
+                     out=None, workspace=None, split_tokens: int = 0, stream=None):
+    """q [B, Hq, D] (f32/bf16/f16, contiguous) -> out [B, Hq, D] float32.
+
+    block_tables int32 [B, max_blocks]; seq_lens int32 [B]; ring_k/ring_v
+    bf16 [B, Hkv, ring_cap, D] with ring_lens int32 [B], or None.
+    """
+    torch = _torch()
+    _dev(q, "q")
+    _dev(kv_pool, "kv_pool", torch.uint8)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if not q.is_contiguous() or q.dim() != 3 or q.shape[2] != cfg.head_dim:
+        raise ValueError(f"q must be contiguous [B, Hq, {cfg.head_dim}]")
+    if kv_pool.dim() != 4 or kv_pool.shape[3] != cfg.slot_size_aligned or not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be contiguous [num_blocks, Hkv, block_size, slot_size_aligned]")
+    bsz, hq, d = q.shape
+    hkv = kv_pool.shape[1]
+    if block_tables.dim() != 2 or block_tables.shape[0] != bsz or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous [B, max_blocks]")
+    if seq_lens.shape != (bsz,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be [B]")
+    ring_cap = 0
+    rk = rv = rl = None
+    if ring_k is not None:
+        _dev(ring_k, "ring_k", torch.bfloat16)
+        _dev(ring_v, "ring_v", torch.bfloat16)
+        _dev(ring_lens, "ring_lens", torch.int32)
+        if ring_k.shape != ring_v.shape or ring_k.dim() != 4 or ring_k.shape[:2] != (bsz, hkv) \
+                or ring_k.shape[3] != d or not ring_k.is_contiguous() or not ring_v.is_contiguous():
+            raise ValueError(f"ring_k/ring_v must be contiguous bf16 [B, {hkv}, ring_cap, {d}]")
+        ring_cap = ring_k.shape[2]
+        rk, rv, rl = ring_k.data_ptr(), ring_v.data_ptr(), ring_lens.data_ptr()
+    if out is None:
+        out = torch.empty((bsz, hq, d), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 like q")
+    need, _ = decode_workspace_size(cfg, bsz, hq, max_seq_len, ring_cap, split_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    s = stream if stream is not None else _stream_ptr(q)
+    _check(_lib.tq_decode_attention(ctypes.byref(cfg), layer_idx, q.data_ptr(), _dtype_code(q), bsz, hq, hkv,
+                                    kv_pool.data_ptr(), kv_pool.shape[0], kv_pool.shape[2],
+                                    block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(),
+                                    max_seq_len, rk, rv, rl, ring_cap, float(softmax_scale), out.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(), split_tokens, s))
+    return out
+
+
+def dequant(cfg: Config, layer_idx: int, kv_pool, slot_ids, k_out=None, v_out=None, stream=None):
+    """slot_ids int64 [n] -> (K_hat, V_hat) float32 [n, Hkv, D] in the original basis."""
+    torch = _torch()
+    _dev(kv_pool, "kv_pool", torch.uint8)
+    _dev(slot_ids, "slot_ids", torch.int64)
+    if kv_pool.dim() != 4 or kv_pool.shape[3] != cfg.slot_size_aligned or not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be contiguous [num_blocks, Hkv, block_size, slot_size_aligned]")
+    n = slot_ids.numel()
+    hkv = kv_pool.shape[1]
+    shape = (n, hkv, cfg.head_dim)
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=torch.float32, device=kv_pool.device)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=torch.float32, device=kv_pool.device)
+    s = stream if stream is not None else _stream_ptr(kv_pool)
+    _check(_lib.tq_dequant(ctypes.byref(cfg), layer_idx, kv_pool.data_ptr(), kv_pool.shape[0], hkv,
+                           kv_pool.shape[2], slot_ids.data_ptr(), n, k_out.data_ptr(), v_out.data_ptr(), s))
+    return k_out, v_out
+
+
+# ----------------------------------------------------------------------------- prepared calls
+
+class _Prepared:
+    """A library call with its arguments marshalled once; calling it issues
+    the same C call again (for tight loops where per-call validation in
+    Python would dominate). The tensors must stay alive and unchanged in
+    shape while the object is used."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != TQ_OK:
+            raise TQError(st, last_error())
+
+
+def prepare_quantize(cfg: Config, layer_idx: int, k, v, slot_mapping, kv_pool, stream=None) -> _Prepared:
+    """Validated once like quantize_append; returns a callable re-issuing it."""
+    quantize_append(cfg, layer_idx, k[:0], v[:0], slot_mapping[:0], kv_pool, stream)  # validates shapes/dtypes
+    torch = _torch()
+    _dev(k, "k"); _dev(v, "v"); _dev(slot_mapping, "slot_mapping", torch.int64)
+    t_count = k.shape[0]
+    hkv = kv_pool.shape[1]
+    if k.dim() != 3 or k.shape[1:] != (hkv, cfg.head_dim) or v.shape != k.shape or slot_mapping.shape != (t_count,):
+        raise ValueError("k, v [T, Hkv, D] and slot_mapping [T] required")
+    s = stream if stream is not None else _stream_ptr(k)
+    args = (ctypes.byref(cfg), layer_idx, k.data_ptr(), v.data_ptr(), _dtype_code(k), t_count, hkv,
+            k.stride(0) if t_count > 1 else hkv * cfg.head_dim, v.stride(0) if t_count > 1 else hkv * cfg.head_dim,
+            slot_mapping.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0], kv_pool.shape[2], s)
+    return _Prepared(_lib.tq_quantize_append, args, (cfg, k, v, slot_mapping, kv_pool))
+
+
+def prepare_decode(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_lens, max_seq_len: int,
+                   ring_k=None, ring_v=None, ring_lens=None, softmax_scale: float = 0.0, out=None,
+                   workspace=None, split_tokens: int = 0, stream=None) -> _Prepared:
+    """Validated once like decode_attention (which it runs once); returns a
+    callable re-issuing the same call into the same out/workspace."""
+    torch = _torch()
+    bsz, hq, d = q.shape
+    ring_cap = 0 if ring_k is None else ring_k.shape[2]
+    need, _ = decode_workspace_size(cfg, bsz, hq, max_seq_len, ring_cap, split_tokens)
+    if out is None:
+        out = torch.empty((bsz, hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    decode_attention(cfg, layer_idx, q, kv_pool, block_tables, seq_lens, max_seq_len, ring_k, ring_v,
+                     ring_lens, softmax_scale, out, workspace, split_tokens, stream)
+    s = stream if stream is not None else _stream_ptr(q)
+    rk = None if ring_k is None else ring_k.data_ptr()
+    rv = None if ring_v is None else ring_v.data_ptr()
+    rl = None if ring_lens is None else ring_lens.data_ptr()
+    args = (ctypes.byref(cfg), layer_idx, q.data_ptr(), _dtype_code(q), bsz, hq, kv_pool.shape[1],
+            kv_pool.data_ptr(), kv_pool.shape[0], kv_pool.shape[2], block_tables.data_ptr(),
+            block_tables.shape[1], seq_lens.data_ptr(), max_seq_len, rk, rv, rl, ring_cap,
+            ctypes.c_float(softmax_scale), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+            split_tokens, s)
+    p = _Prepared(_lib.tq_decode_attention, args,
+                  (cfg, q, kv_pool, block_tables, seq_lens, ring_k, ring_v, ring_lens, out, workspace))
+    p.out = out
+    p.workspace = workspace
+    return p

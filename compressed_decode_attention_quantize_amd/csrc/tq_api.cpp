@@ -1,0 +1,164 @@
+// C ABI entry points that launch GPU work: argument validation on the host,
+// parameter packing, then the launchers in the kernel translation units.
+// Nothing is enqueued when validation fails.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "tq_internal.h"
+
+using namespace tq;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+tq_status hip_fail(const char *what, int err) {
+  return fail(TQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(static_cast<hipError_t>(err)));
+}
+
+bool valid_dtype(tq_dtype d) { return d == TQ_F32 || d == TQ_BF16 || d == TQ_F16; }
+
+}  // namespace
+
+TQ_EXPORT tq_status tq_quantize_append(const tq_config *cfg, int layer_idx, const void *k, const void *v,
+                                       tq_dtype in_dtype, int64_t num_tokens, int num_kv_heads,
+                                       int64_t k_token_stride, int64_t v_token_stride,
+                                       const int64_t *slot_mapping, uint8_t *kv_pool, int64_t num_blocks,
+                                       int block_size, void *stream) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0 || block_size <= 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: negative num_tokens/num_blocks or non-positive heads/block_size");
+  if (!valid_dtype(in_dtype)) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: unknown input dtype");
+  if (num_tokens == 0) return TQ_OK;
+  if (!k || !v || !slot_mapping || !kv_pool) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: NULL pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(kv_pool))
+    return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: k, v and kv_pool must be 16-byte aligned");
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * cfg->head_dim;
+  if (k_token_stride < row || v_token_stride < row || k_token_stride % 8 || v_token_stride % 8)
+    return fail(TQ_ERR_INVALID_ARG,
+                "tq_quantize_append: token strides must be >= num_kv_heads*head_dim and multiples of 8 elements");
+  QuantParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.k = k;
+  p.v = v;
+  p.slot_mapping = slot_mapping;
+  p.pool = kv_pool;
+  p.num_tokens = num_tokens;
+  p.k_stride = k_token_stride;
+  p.v_stride = v_token_stride;
+  p.total_slots = num_blocks * block_size;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.slot_bytes = cfg->slot_size_aligned;
+  p.key_bytes = cfg->key_packed_size;
+  layer_sign_mask(*cfg, layer_idx, p.sign_words);
+  for (int i = 0; i < 15; ++i) p.midpoints[i] = cfg->midpoints[i];
+  p.sqrt_block = static_cast<float>(std::sqrt(static_cast<double>(cfg->wht_block)));
+  const int err = launch_quantize(*cfg, in_dtype, p, stream);
+  if (err != hipSuccess) return hip_fail("tq_quantize_append launch", err);
+  return TQ_OK;
+}
+
+TQ_EXPORT tq_status tq_dequant(const tq_config *cfg, int layer_idx, const uint8_t *kv_pool, int64_t num_blocks,
+                               int num_kv_heads, int block_size, const int64_t *slot_ids, int64_t n,
+                               float *k_out, float *v_out, void *stream) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (n < 0 || num_kv_heads <= 0 || num_blocks < 0 || block_size <= 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_dequant: negative n/num_blocks or non-positive heads/block_size");
+  if (n == 0) return TQ_OK;
+  if (!kv_pool || !slot_ids || !k_out || !v_out) return fail(TQ_ERR_INVALID_ARG, "tq_dequant: NULL pointer");
+  if (!aligned16(k_out) || !aligned16(v_out)) return fail(TQ_ERR_INVALID_ARG, "tq_dequant: outputs must be 16-byte aligned");
+  DequantParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.pool = kv_pool;
+  p.slot_ids = slot_ids;
+  p.k_out = k_out;
+  p.v_out = v_out;
+  p.n = n;
+  p.total_slots = num_blocks * block_size;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.slot_bytes = cfg->slot_size_aligned;
+  p.key_bytes = cfg->key_packed_size;
+  p.norm_correction = cfg->norm_correction;
+  layer_sign_mask(*cfg, layer_idx, p.sign_words);
+  for (int i = 0; i < 16; ++i) p.centroids[i] = cfg->centroids[i];
+  p.inv_sqrt_block = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cfg->wht_block)));
+  const int err = launch_dequant(*cfg, p, stream);
+  if (err != hipSuccess) return hip_fail("tq_dequant launch", err);
+  return TQ_OK;
+}
+
+TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, const void *q, tq_dtype q_dtype,
+                                        int batch, int num_q_heads, int num_kv_heads, const uint8_t *kv_pool,
+                                        int64_t num_blocks, int block_size, const int32_t *block_tables,
+                                        int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len,
+                                        const void *ring_k, const void *ring_v, const int32_t *ring_lens,
+                                        int ring_cap, float softmax_scale, float *out, void *workspace,
+                                        size_t workspace_bytes, int split_tokens, void *stream) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: need batch >= 0 and num_q_heads a positive multiple of num_kv_heads");
+  if (num_q_heads / num_kv_heads > 16)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: at most 16 query heads per KV head");
+  if (block_size <= 0 || block_size % 16 != 0)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: block_size must be a positive multiple of 16");
+  if (max_seq_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0 || ring_cap < 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: negative size argument");
+  if (!valid_dtype(q_dtype)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: unknown q dtype");
+  const bool has_ring = ring_k != nullptr || ring_v != nullptr;
+  if (has_ring && (!ring_k || !ring_v || !ring_lens || ring_cap <= 0))
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: ring needs ring_k, ring_v, ring_lens and ring_cap > 0");
+  if (!has_ring && ring_cap != 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: ring_cap must be 0 without a ring");
+  if (batch == 0) return TQ_OK;
+  if (!q || !kv_pool || !block_tables || !seq_lens || !out)
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: NULL pointer");
+  if (!aligned16(kv_pool)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: kv_pool must be 16-byte aligned");
+  SplitPlan plan;
+  st = plan_decode(*cfg, batch, num_q_heads, max_seq_len, ring_cap, split_tokens, &plan);
+  if (st != TQ_OK) return st;
+  if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned16(workspace))
+    return fail(TQ_ERR_WORKSPACE, "tq_decode_attention: workspace must be 16-byte aligned and hold " +
+                                      std::to_string(plan.workspace_bytes) + " bytes");
+  DecodeParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.pool = kv_pool;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.ring_k = static_cast<const uint16_t *>(ring_k);
+  p.ring_v = static_cast<const uint16_t *>(ring_v);
+  p.ring_lens = ring_lens;
+  p.partials = static_cast<float *>(workspace);
+  p.out = out;
+  p.num_blocks = num_blocks;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
+  p.ring_cap = has_ring ? ring_cap : 0;
+  p.split_tokens = plan.split_tokens;
+  p.num_splits = plan.num_splits;
+  p.splits_total = plan.splits_total;
+  p.slot_bytes = cfg->slot_size_aligned;
+  p.key_bytes = cfg->key_packed_size;
+  p.norm_correction = cfg->norm_correction;
+  const float scale = softmax_scale > 0.0f ? softmax_scale
+                                           : static_cast<float>(1.0 / std::sqrt(static_cast<double>(cfg->head_dim)));
+  p.scale_log2 = scale * 1.4426950408889634f;
+  layer_sign_mask(*cfg, layer_idx, p.sign_words);
+  for (int i = 0; i < 16; ++i) p.centroids[i] = cfg->centroids[i];
+  const int err = launch_decode(*cfg, q_dtype, p, stream);
+  if (err != hipSuccess) return hip_fail("tq_decode_attention launch", err);
+  return TQ_OK;
+}

@@ -1,0 +1,235 @@
+// Host core of the library: configuration (TurboQuantConfig arithmetic),
+// Lloyd-Max tables, per-layer random signs, the decode split plan, and the
+// thread-local error message. No HIP calls here.
+//
+// Sources: vLLM API page "vllm.model_executor.layers.quantization.turboquant",
+// TurboQuantConfig (fields, properties, named presets, from_cache_dtype);
+// prhub summary of vLLM PR #39931 (TurboQuant page = block_size *
+// num_kv_heads * slot bytes).
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+namespace {
+thread_local std::string g_last_error;
+
+struct Preset {
+  const char *name;
+  int key_bits, value_bits, nc;
+};
+// In the order the TurboQuantConfig docstring lists them.
+constexpr Preset kPresets[] = {
+    {"turboquant_k8v4", 8, 4, 0},
+    {"turboquant_4bit_nc", 4, 4, 1},
+    {"turboquant_k3v4_nc", 3, 4, 1},
+    {"turboquant_3bit_nc", 3, 3, 1},
+};
+
+int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Lloyd-Max quantizer of the standard normal (Lloyd's fixed-point iteration:
+// thresholds at the midpoints of adjacent levels, each level the mean of the
+// density over its cell). The positive half is iterated and mirrored, so the
+// table is exactly antisymmetric. float64.
+constexpr int kLloydIterations = 2000;
+
+double normal_cell_mean(double a, double b) {  // 0 <= a < b <= inf
+  const double inv_sqrt_2pi = 1.0 / std::sqrt(2.0 * M_PI);
+  const double pa = std::exp(-0.5 * a * a) * inv_sqrt_2pi;
+  const double pb = std::isinf(b) ? 0.0 : std::exp(-0.5 * b * b) * inv_sqrt_2pi;
+  const double ea = std::erfc(a / std::sqrt(2.0));
+  const double eb = std::isinf(b) ? 0.0 : std::erfc(b / std::sqrt(2.0));
+  return (pa - pb) / (0.5 * (ea - eb));
+}
+
+void standard_normal_levels(int levels, double *out) {
+  const int half = levels / 2;
+  double c[8], edge[9];
+  for (int k = 0; k < half; ++k) c[k] = (k + 0.5) * 3.0 / half;
+  for (int it = 0; it < kLloydIterations; ++it) {
+    edge[0] = 0.0;
+    for (int k = 1; k < half; ++k) edge[k] = (c[k - 1] + c[k]) / 2.0;
+    edge[half] = INFINITY;
+    for (int k = 0; k < half; ++k) c[k] = normal_cell_mean(edge[k], edge[k + 1]);
+  }
+  for (int k = 0; k < half; ++k) {
+    out[half + k] = c[k];
+    out[half - 1 - k] = -c[k];
+  }
+}
+
+// SplitMix64 (Steele, Lea and Flood 2014), one step.
+uint64_t splitmix64_next(uint64_t &state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+bool supported_head_dim(int d) { return d == 64 || d == 96 || d == 128; }
+
+}  // namespace
+
+tq_status fail(tq_status st, const std::string &msg) {
+  g_last_error = msg;
+  return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+tq_status check_config(const tq_config *cfg) {
+  if (!cfg) return fail(TQ_ERR_INVALID_ARG, "config is NULL");
+  tq_config ref;
+  if (tq_config_init(cfg->head_dim, cfg->key_quant_bits, cfg->value_quant_bits,
+                     cfg->norm_correction, cfg->seed, &ref) != TQ_OK)
+    return TQ_ERR_INVALID_ARG;
+  if (ref.slot_size_aligned != cfg->slot_size_aligned || ref.key_packed_size != cfg->key_packed_size ||
+      ref.value_packed_size != cfg->value_packed_size || ref.wht_block != cfg->wht_block ||
+      ref.key_fp8 != cfg->key_fp8 || ref.n_centroids != cfg->n_centroids)
+    return fail(TQ_ERR_INVALID_ARG, "config was modified after tq_config_init");
+  clear_error();
+  return TQ_OK;
+}
+
+void layer_sign_mask(const tq_config &cfg, int layer_idx, uint32_t words[4]) {
+  uint64_t state = static_cast<uint64_t>(cfg.seed) + static_cast<uint64_t>(layer_idx) * 1337ull;
+  words[0] = words[1] = words[2] = words[3] = 0;
+  for (int j = 0; j < cfg.head_dim; ++j) {
+    const uint64_t z = splitmix64_next(state);
+    if (z >> 63) words[j >> 5] |= 1u << (j & 31);
+  }
+}
+
+tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_seq_len,
+                      int ring_cap, int split_tokens, SplitPlan *plan) {
+  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || ring_cap < 0)
+    return fail(TQ_ERR_INVALID_ARG, "decode plan: negative batch/max_seq_len/ring_cap or num_q_heads <= 0");
+  int st = split_tokens;
+  if (st < 0 || st % 16 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "split_tokens must be 0 (auto) or a positive multiple of 16");
+  if (st == 0) {
+    // Aim for about 4096 (sequence, KV head, split) work items assuming 8 KV
+    // heads, with 256..2048 tokens per split.
+    const long long want_splits = std::max(1LL, (4096LL + 8LL * std::max(batch, 1) - 1) / (8LL * std::max(batch, 1)));
+    long long per = (max_seq_len + want_splits - 1) / want_splits;
+    per = ((per + 63) / 64) * 64;
+    if (per < 256) per = 256;
+    if (per > 2048) per = 2048;
+    st = static_cast<int>(per);
+  }
+  plan->split_tokens = st;
+  plan->num_splits = max_seq_len > 0 ? ceil_div_i(max_seq_len, st) : 0;
+  plan->splits_total = plan->num_splits + (ring_cap > 0 ? 1 : 0);
+  if (plan->splits_total == 0) plan->splits_total = 1;  // empty context still writes zeros
+  plan->workspace_bytes = static_cast<size_t>(batch) * num_q_heads * plan->splits_total *
+                          (cfg.head_dim + 2) * sizeof(float);
+  return TQ_OK;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+TQ_EXPORT tq_status tq_config_init(int head_dim, int key_bits, int value_bits, int norm_correction,
+                                   int64_t seed, tq_config *out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_config_init: out is NULL");
+  if (!supported_head_dim(head_dim))
+    return fail(TQ_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) + " not supported (64, 96, 128)");
+  if (key_bits != 3 && key_bits != 4 && key_bits != 8)
+    return fail(TQ_ERR_INVALID_ARG, "key_quant_bits must be 3, 4 (MSE) or 8 (FP8), got " + std::to_string(key_bits));
+  if (value_bits != 3 && value_bits != 4)
+    return fail(TQ_ERR_INVALID_ARG, "value_quant_bits must be 3 or 4, got " + std::to_string(value_bits));
+  tq_config c;
+  std::memset(&c, 0, sizeof(c));
+  c.head_dim = head_dim;
+  c.key_quant_bits = key_bits;
+  c.value_quant_bits = value_bits;
+  c.norm_correction = norm_correction ? 1 : 0;
+  c.seed = seed;
+  // Derived properties, as the printed TurboQuantConfig properties compute them.
+  c.key_fp8 = key_bits == 8;
+  c.mse_bits = c.key_fp8 ? value_bits : key_bits;
+  c.key_mse_bits = c.key_fp8 ? 0 : key_bits;
+  c.centroid_bits = c.mse_bits;
+  c.n_centroids = 1 << c.mse_bits;
+  c.key_packed_size = c.key_fp8 ? head_dim : ceil_div_i(head_dim * c.key_mse_bits, 8) + 2;
+  c.value_packed_size = ceil_div_i(head_dim * value_bits, 8) + 4;
+  c.slot_size = c.key_packed_size + c.value_packed_size;
+  c.slot_size_aligned = c.slot_size + (c.slot_size % 2);
+  c.wht_block = head_dim & (-head_dim);
+  // Lloyd-Max table of N(0, 1/D): the standard-normal levels scaled by 1/sqrt(D).
+  double lv[16];
+  standard_normal_levels(c.n_centroids, lv);
+  const double sd = std::sqrt(static_cast<double>(head_dim));
+  double c64[16];
+  for (int k = 0; k < c.n_centroids; ++k) {
+    c64[k] = lv[k] / sd;
+    c.centroids[k] = static_cast<float>(c64[k]);
+  }
+  for (int k = 0; k + 1 < c.n_centroids; ++k) c.midpoints[k] = static_cast<float>((c64[k] + c64[k + 1]) / 2.0);
+  *out = c;
+  clear_error();
+  return TQ_OK;
+}
+
+TQ_EXPORT tq_status tq_config_from_preset(const char *preset, int head_dim, tq_config *out) {
+  if (!preset || !out) return fail(TQ_ERR_INVALID_ARG, "tq_config_from_preset: NULL argument");
+  for (const Preset &p : kPresets)
+    if (std::strcmp(p.name, preset) == 0) return tq_config_init(head_dim, p.key_bits, p.value_bits, p.nc, 42, out);
+  std::string valid;
+  for (const Preset &p : kPresets) {
+    if (!valid.empty()) valid += ", ";
+    valid += p.name;
+  }
+  return fail(TQ_ERR_UNKNOWN_PRESET,
+              std::string("Unknown TurboQuant cache dtype: '") + preset + "'. Valid presets: " + valid);
+}
+
+TQ_EXPORT int32_t tq_slot_size(const tq_config *cfg, int aligned) {
+  if (check_config(cfg) != TQ_OK) return -1;
+  return aligned ? cfg->slot_size_aligned : cfg->slot_size;
+}
+
+TQ_EXPORT int64_t tq_page_size(const tq_config *cfg, int num_kv_heads, int block_size) {
+  if (check_config(cfg) != TQ_OK) return -1;
+  if (num_kv_heads <= 0 || block_size <= 0) {
+    fail(TQ_ERR_INVALID_ARG, "tq_page_size: num_kv_heads and block_size must be positive");
+    return -1;
+  }
+  return static_cast<int64_t>(block_size) * num_kv_heads * cfg->slot_size_aligned;
+}
+
+TQ_EXPORT tq_status tq_layer_signs(const tq_config *cfg, int layer_idx, float *signs_out) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (!signs_out) return fail(TQ_ERR_INVALID_ARG, "tq_layer_signs: signs_out is NULL");
+  uint32_t w[4];
+  layer_sign_mask(*cfg, layer_idx, w);
+  for (int j = 0; j < cfg->head_dim; ++j) signs_out[j] = ((w[j >> 5] >> (j & 31)) & 1u) ? -1.0f : 1.0f;
+  return TQ_OK;
+}
+
+TQ_EXPORT tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, int num_q_heads,
+                                             int max_seq_len, int ring_cap, int split_tokens,
+                                             size_t *bytes_out, int *num_splits_out) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (!bytes_out) return fail(TQ_ERR_INVALID_ARG, "tq_decode_workspace_size: bytes_out is NULL");
+  SplitPlan plan;
+  st = plan_decode(*cfg, batch, num_q_heads, max_seq_len, ring_cap, split_tokens, &plan);
+  if (st != TQ_OK) return st;
+  *bytes_out = plan.workspace_bytes;
+  if (num_splits_out) *num_splits_out = plan.splits_total;
+  return TQ_OK;
+}
+
+TQ_EXPORT const char *tq_last_error(void) { return g_last_error.c_str(); }
+
+TQ_EXPORT const char *tq_version(void) { return "tq-mi355x 0.1.0 gfx950"; }

@@ -1,0 +1,107 @@
+// Internal declarations shared by the host core, the C-ABI layer and the
+// kernel translation units. Not installed; the public surface is include/tq.h.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/tq.h"
+
+#define TQ_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace tq {
+
+// Records the message returned by tq_last_error() on this thread and returns
+// the status, so call sites can write `return fail(TQ_ERR_..., "...")`.
+tq_status fail(tq_status st, const std::string &msg);
+void clear_error();
+
+// Validates a config filled by tq_config_init (recomputes the derived sizes).
+tq_status check_config(const tq_config *cfg);
+
+// Random signs of one layer as a bit mask: bit j of words[j / 32] is set when
+// sign j is -1. head_dim <= 128.
+void layer_sign_mask(const tq_config &cfg, int layer_idx, uint32_t words[4]);
+
+// Kernel parameter blocks. Plain structs passed by value to the kernels.
+struct QuantParams {
+  const void *k;
+  const void *v;
+  const int64_t *slot_mapping;
+  uint8_t *pool;
+  int64_t num_tokens;
+  int64_t k_stride;     // elements
+  int64_t v_stride;     // elements
+  int64_t total_slots;  // num_blocks * block_size
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t slot_bytes;   // slot_size_aligned
+  int32_t key_bytes;    // key_packed_size
+  uint32_t sign_words[4];
+  float midpoints[15];
+  float sqrt_block;     // fp32(sqrt(B))
+};
+
+struct DequantParams {
+  const uint8_t *pool;
+  const int64_t *slot_ids;
+  float *k_out;
+  float *v_out;
+  int64_t n;
+  int64_t total_slots;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t slot_bytes;
+  int32_t key_bytes;
+  int32_t norm_correction;
+  uint32_t sign_words[4];
+  float centroids[16];
+  float inv_sqrt_block;  // fp32(1/sqrt(B))
+};
+
+struct DecodeParams {
+  const void *q;
+  const uint8_t *pool;
+  const int32_t *block_tables;
+  const int32_t *seq_lens;
+  const uint16_t *ring_k;  // bf16 bits
+  const uint16_t *ring_v;
+  const int32_t *ring_lens;
+  float *partials;         // [batch][Hq][splits_total][D + 2]
+  float *out;
+  int64_t num_blocks;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t max_seq_len;
+  int32_t ring_cap;
+  int32_t split_tokens;    // compressed tokens per split, multiple of 16
+  int32_t num_splits;      // compressed splits per sequence
+  int32_t splits_total;    // num_splits + (ring ? 1 : 0)
+  int32_t slot_bytes;
+  int32_t key_bytes;
+  int32_t norm_correction;
+  float scale_log2;        // softmax scale * log2(e)
+  uint32_t sign_words[4];
+  float centroids[16];
+};
+
+// Launchers (defined in the kernel translation units). Return hipSuccess or a
+// HIP error code as int.
+int launch_quantize(const tq_config &cfg, tq_dtype dtype, const QuantParams &p, void *stream);
+int launch_dequant(const tq_config &cfg, const DequantParams &p, void *stream);
+int launch_decode(const tq_config &cfg, tq_dtype q_dtype, const DecodeParams &p, void *stream);
+
+// Split plan shared by tq_decode_workspace_size and tq_decode_attention.
+struct SplitPlan {
+  int32_t split_tokens;
+  int32_t num_splits;
+  int32_t splits_total;
+  size_t workspace_bytes;
+};
+tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_seq_len,
+                      int ring_cap, int split_tokens, SplitPlan *plan);
+
+}  // namespace tq

@@ -1,0 +1,301 @@
+// Quantize-and-append and dequant kernels.
+//
+// Sources: vLLM API page "vllm.model_executor.layers.quantization.turboquant",
+// TurboQuantConfig docstring (Walsh-Hadamard rotation + Lloyd-Max keys,
+// uniform values, FP8 keys, norm correction at dequant) and the byte layouts
+// of key_packed_size / value_packed_size / slot_size.
+//
+// Layout of the work: one (token, head) vector is handled by a team of D/8
+// lanes holding 8 consecutive elements each (see Team<D>), so the rotation is
+// in-register butterflies plus lane-xor exchanges and the norm / min / max
+// are lane reductions. fp32 op order is fixed (the library is built with
+// -ffp-contract=off; sqrt and divide are correctly rounded) so the bytes
+// match the CPU oracle exactly.
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Write `nbytes` (<= 4) little-endian bytes of w at dst (any alignment).
+__device__ __forceinline__ void store_bytes(uint8_t *dst, uint32_t w, int nbytes) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < nbytes) dst[i] = static_cast<uint8_t>(w >> (8 * i));
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t pack8(const uint32_t c[8]) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= c[i] << (BITS * i);
+  return w;
+}
+
+template <int BITS>
+__device__ __forceinline__ void unpack8(uint32_t w, uint32_t c[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = (w >> (BITS * i)) & ((1u << BITS) - 1u);
+}
+
+// Reads the BITS*8-bit group of lane r from a packed field (byte aligned).
+template <int BITS>
+__device__ __forceinline__ uint32_t load_group(const uint8_t *field, int r) {
+  const uint8_t *p = field + BITS * r;
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) w |= static_cast<uint32_t>(p[i]) << (8 * i);
+  return w;
+}
+
+template <int D, int KB, int VB, int DT>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
+  using T = Team<D>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int team = lane / T::kLanes;
+  const int r = lane - team * T::kLanes;           // lane within the team
+  const int team_base = team * T::kLanes;
+  const int lane_in_block = r % T::kBlockLanes;
+  const int64_t vec = (static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave) * T::kPerWave + team;
+  const int64_t nvec = p.num_tokens * p.num_kv_heads;
+  const bool active = team < T::kPerWave && vec < nvec;
+  const int64_t t = active ? vec / p.num_kv_heads : 0;
+  const int h = active ? static_cast<int>(vec - t * p.num_kv_heads) : 0;
+
+  float x[8], v[8];
+  if (active) {
+    load8<DT>(p.k, t * p.k_stride + static_cast<int64_t>(h) * D + 8 * r, x);
+    load8<DT>(p.v, t * p.v_stride + static_cast<int64_t>(h) * D + 8 * r, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = v[i] = 0.0f;
+  }
+  int64_t slot = active ? p.slot_mapping[t] : -1;
+  const bool write = active && slot >= 0 && slot < p.total_slots;
+  if (!write) slot = 0;
+  const int64_t blk = slot / p.block_size;
+  const int64_t off = slot - blk * p.block_size;
+  uint8_t *dst = p.pool + ((blk * p.num_kv_heads + h) * p.block_size + off) * p.slot_bytes;
+
+  // ---- keys
+  if constexpr (KB == 8) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= float_to_e4m3fn(x[i]) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= float_to_e4m3fn(x[4 + i]) << (8 * i);
+    if (write) {
+      store_bytes(dst + 8 * r, lo, 4);
+      store_bytes(dst + 8 * r + 4, hi, 4);
+    }
+  } else {
+    const float n2 = team_sumsq<D>(x, team_base);
+    const float n = sqrtf(n2);
+    const uint32_t sbits = lane_sign_bits(p.sign_words, r);
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = flip_sign(x[i], (sbits >> i) & 1u);
+    team_wht<D>(z, lane_in_block);
+    const float pn = n * p.sqrt_block;
+    const float rcp = (n == 0.0f) ? 0.0f : 1.0f / pn;
+    uint32_t idx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float u = z[i] * rcp;
+      uint32_t c = 0;
+#pragma unroll
+      for (int k = 0; k < (1 << KB) - 1; ++k) c += (u > p.midpoints[k]) ? 1u : 0u;
+      idx[i] = c;
+    }
+    const uint32_t w = pack8<KB>(idx);
+    if (write) {
+      store_bytes(dst + KB * r, w, KB);
+      if (r == 0) store_bytes(dst + (D * KB) / 8, float_to_f16_bits(n), 2);
+    }
+  }
+
+  // ---- values
+  float mn = v[0], mx = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    mn = fminf(mn, v[i]);
+    mx = fmaxf(mx, v[i]);
+  }
+  mn = team_min<D>(mn, team_base);
+  mx = team_max<D>(mx, team_base);
+  constexpr float kLevels = static_cast<float>((1 << VB) - 1);
+  const float scale32 = (mx - mn) / kLevels;
+  const uint32_t s16 = float_to_f16_bits(scale32);
+  const uint32_t z16 = float_to_f16_bits(mn);
+  const float s1 = f16_bits_to_float(s16);
+  const float z1 = f16_bits_to_float(z16);
+  const float inv = (s1 == 0.0f) ? 0.0f : 1.0f / s1;
+  uint32_t code[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float qv = rintf((v[i] - z1) * inv);
+    code[i] = static_cast<uint32_t>(fminf(fmaxf(qv, 0.0f), kLevels));
+  }
+  const uint32_t wv = pack8<VB>(code);
+  if (write) {
+    uint8_t *vf = dst + p.key_bytes;
+    store_bytes(vf + VB * r, wv, VB);
+    if (r == 0) {
+      store_bytes(vf + (D * VB) / 8, s16, 2);
+      store_bytes(vf + (D * VB) / 8 + 2, z16, 2);
+      if (p.slot_bytes > p.key_bytes + (D * VB) / 8 + 4) dst[p.slot_bytes - 1] = 0;
+    }
+  }
+}
+
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantParams p) {
+  using T = Team<D>;
+  __shared__ float cent[16];
+  if (threadIdx.x < 16) cent[threadIdx.x] = p.centroids[threadIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int team = lane / T::kLanes;
+  const int r = lane - team * T::kLanes;
+  const int team_base = team * T::kLanes;
+  const int lane_in_block = r % T::kBlockLanes;
+  const int64_t vec = (static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave) * T::kPerWave + team;
+  const int64_t nvec = p.n * p.num_kv_heads;
+  const bool active = team < T::kPerWave && vec < nvec;
+  const int64_t i = active ? vec / p.num_kv_heads : 0;
+  const int h = active ? static_cast<int>(vec - i * p.num_kv_heads) : 0;
+  int64_t slot = active ? p.slot_ids[i] : -1;
+  const bool valid = active && slot >= 0 && slot < p.total_slots;
+  if (!valid) slot = 0;
+  const int64_t blk = slot / p.block_size;
+  const int64_t off = slot - blk * p.block_size;
+  const uint8_t *src = p.pool + ((blk * p.num_kv_heads + h) * p.block_size + off) * p.slot_bytes;
+
+  float k[8], v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) k[e] = v[e] = 0.0f;
+  // validity is uniform over a team, so the team's lane exchanges stay paired
+  if (valid) {
+  if constexpr (KB == 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) k[e] = e4m3fn_to_float(src[8 * r + e]);
+  } else {
+    uint32_t idx[8];
+    unpack8<KB>(load_group<KB>(src, r), idx);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = cent[idx[e]];
+    if (p.norm_correction) {
+      const float cn = sqrtf(team_sumsq<D>(y, team_base));
+      const float inv = 1.0f / cn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = y[e] * inv;
+    }
+    team_wht<D>(y, lane_in_block);
+    const uint32_t nb = static_cast<uint32_t>(src[(D * KB) / 8]) | (static_cast<uint32_t>(src[(D * KB) / 8 + 1]) << 8);
+    const float fac = f16_bits_to_float(nb) * p.inv_sqrt_block;
+    const uint32_t sbits = lane_sign_bits(p.sign_words, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) k[e] = flip_sign(y[e] * fac, (sbits >> e) & 1u);
+  }
+  {
+    const uint8_t *vf = src + p.key_bytes;
+    uint32_t code[8];
+    unpack8<VB>(load_group<VB>(vf, r), code);
+    const uint32_t sb = static_cast<uint32_t>(vf[(D * VB) / 8]) | (static_cast<uint32_t>(vf[(D * VB) / 8 + 1]) << 8);
+    const uint32_t zb = static_cast<uint32_t>(vf[(D * VB) / 8 + 2]) | (static_cast<uint32_t>(vf[(D * VB) / 8 + 3]) << 8);
+    const float s1 = f16_bits_to_float(sb), z1 = f16_bits_to_float(zb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (s1 * static_cast<float>(code[e])) + z1;
+  }
+  }  // valid
+  if (!active) return;
+  float4 *ko = reinterpret_cast<float4 *>(p.k_out + (i * p.num_kv_heads + h) * D + 8 * r);
+  float4 *vo = reinterpret_cast<float4 *>(p.v_out + (i * p.num_kv_heads + h) * D + 8 * r);
+  ko[0] = make_float4(k[0], k[1], k[2], k[3]);
+  ko[1] = make_float4(k[4], k[5], k[6], k[7]);
+  vo[0] = make_float4(v[0], v[1], v[2], v[3]);
+  vo[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <int D, int KB, int VB>
+int launch_quantize_t(tq_dtype dt, const QuantParams &p, hipStream_t s) {
+  using T = Team<D>;
+  const int64_t nvec = p.num_tokens * p.num_kv_heads;
+  const int64_t per_block = (kThreads / 64) * T::kPerWave;
+  const int64_t blocks = (nvec + per_block - 1) / per_block;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (dt) {
+    case TQ_F32: hipLaunchKernelGGL((quantize_kernel<D, KB, VB, 0>), grid, dim3(kThreads), 0, s, p); break;
+    case TQ_BF16: hipLaunchKernelGGL((quantize_kernel<D, KB, VB, 1>), grid, dim3(kThreads), 0, s, p); break;
+    case TQ_F16: hipLaunchKernelGGL((quantize_kernel<D, KB, VB, 2>), grid, dim3(kThreads), 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
+template <int D, int KB, int VB>
+int launch_dequant_t(const DequantParams &p, hipStream_t s) {
+  using T = Team<D>;
+  const int64_t nvec = p.n * p.num_kv_heads;
+  const int64_t per_block = (kThreads / 64) * T::kPerWave;
+  const int64_t blocks = (nvec + per_block - 1) / per_block;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((dequant_kernel<D, KB, VB>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+int dispatch_quantize_bits(const tq_config &c, tq_dtype dt, const QuantParams &p, hipStream_t s) {
+  const int kb = c.key_quant_bits, vb = c.value_quant_bits;
+  if (kb == 3 && vb == 3) return launch_quantize_t<D, 3, 3>(dt, p, s);
+  if (kb == 3 && vb == 4) return launch_quantize_t<D, 3, 4>(dt, p, s);
+  if (kb == 4 && vb == 3) return launch_quantize_t<D, 4, 3>(dt, p, s);
+  if (kb == 4 && vb == 4) return launch_quantize_t<D, 4, 4>(dt, p, s);
+  if (kb == 8 && vb == 3) return launch_quantize_t<D, 8, 3>(dt, p, s);
+  if (kb == 8 && vb == 4) return launch_quantize_t<D, 8, 4>(dt, p, s);
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+int dispatch_dequant_bits(const tq_config &c, const DequantParams &p, hipStream_t s) {
+  const int kb = c.key_quant_bits, vb = c.value_quant_bits;
+  if (kb == 3 && vb == 3) return launch_dequant_t<D, 3, 3>(p, s);
+  if (kb == 3 && vb == 4) return launch_dequant_t<D, 3, 4>(p, s);
+  if (kb == 4 && vb == 3) return launch_dequant_t<D, 4, 3>(p, s);
+  if (kb == 4 && vb == 4) return launch_dequant_t<D, 4, 4>(p, s);
+  if (kb == 8 && vb == 3) return launch_dequant_t<D, 8, 3>(p, s);
+  if (kb == 8 && vb == 4) return launch_dequant_t<D, 8, 4>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int launch_quantize(const tq_config &c, tq_dtype dt, const QuantParams &p, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (c.head_dim) {
+    case 64: return dispatch_quantize_bits<64>(c, dt, p, s);
+    case 96: return dispatch_quantize_bits<96>(c, dt, p, s);
+    case 128: return dispatch_quantize_bits<128>(c, dt, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+int launch_dequant(const tq_config &c, const DequantParams &p, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (c.head_dim) {
+    case 64: return dispatch_dequant_bits<64>(c, p, s);
+    case 96: return dispatch_dequant_bits<96>(c, p, s);
+    case 128: return dispatch_dequant_bits<128>(c, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

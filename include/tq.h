@@ -1,0 +1,230 @@
+/*
+ * tq.h -- C ABI of the TurboQuant KV-cache hot path for AMD Instinct MI355X
+ * (gfx950): quantize-and-append K/V into packed per-head slots, and fused
+ * decode attention directly over those slots.
+ *
+ * Sources the operations follow (cited by page and section):
+ *  [API]  vLLM API page "vllm.model_executor.layers.quantization.turboquant",
+ *         class TurboQuantConfig: docstring, fields, properties,
+ *         from_cache_dtype.
+ *  [PR]   prhub summary of vLLM PR #39931, "TurboQuant supports hybrid models
+ *         and fixes page-size alignment", interface.py source snippet
+ *         (TurboQuant page size = block_size * num_kv_heads * slot bytes).
+ *  [ART]  hnwysp.cn article on the stand-alone turboquant project (full_tq
+ *         zero-allocation mode): write-path section (128-token bf16 exact
+ *         ring buffer, whole-chunk compression) and next-directions
+ *         section, direction 1 (fused decode attention: single pass over the
+ *         compressed data, online softmax block by block, query rotated
+ *         forward instead of rotating keys back, no materialised FP16 KV).
+ *
+ * Conventions for every function:
+ *  - Returns a tq_status; never throws or aborts. On failure nothing is
+ *    enqueued and tq_last_error() describes the problem.
+ *  - Device pointers are caller-owned; the library allocates no device memory
+ *    and keeps no mutable global state, so calls are reentrant and may run
+ *    concurrently on different streams when they write disjoint memory.
+ *  - GPU calls are asynchronous and ordered on `stream` (a hipStream_t passed
+ *    as void*; NULL = the default stream).
+ *  - Scalars and null pointers are validated on the host. Device contents
+ *    (slot ids, block ids, lengths) are clamped or skipped by the kernels so
+ *    that bad values cannot make them read or write out of bounds; such
+ *    values give unspecified results, not faults.
+ *  - Pool layout: uint8 [num_blocks][num_kv_heads][block_size][S] with
+ *    S = slot_size_aligned; token position p of a sequence lives in physical
+ *    block block_table[p / block_size] at offset p % block_size. The page of
+ *    one block is block_size * num_kv_heads * S bytes ([PR]); the order inside
+ *    it is this library's choice.
+ *  - Slot layout ([API] slot_size): [key_packed | value_packed] where
+ *    key_packed = MSE indices (LSB-first bitstream, ceil(D*kb/8) bytes) +
+ *    fp16 vec_norm, or D FP8 E4M3FN bytes when key_quant_bits == 8; and
+ *    value_packed = codes (LSB-first, ceil(D*vb/8) bytes) + fp16 scale +
+ *    fp16 zero; fp16 fields little-endian; padded to an even size.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1,    /* bad scalar, null pointer, misaligned pointer  */
+  TQ_ERR_UNKNOWN_PRESET = 2, /* tq_config_from_preset with an unknown name    */
+  TQ_ERR_UNSUPPORTED = 3,    /* valid but not built (e.g. head_dim 256)       */
+  TQ_ERR_WORKSPACE = 4,      /* decode workspace missing or too small         */
+  TQ_ERR_HIP = 5             /* a HIP launch or runtime call failed           */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+/*
+ * Configuration: the five dataclass fields of TurboQuantConfig ([API]) plus
+ * the derived properties, computed exactly as the printed properties do, and
+ * the Lloyd-Max tables. A value type filled by tq_config_init or
+ * tq_config_from_preset; callers must not edit it afterwards.
+ *
+ * centroids: the 2^mse_bits Lloyd-Max reconstruction levels of N(0, 1/D),
+ *   ascending, fp32 (rounded from float64; exactly antisymmetric).
+ * midpoints: the 2^mse_bits - 1 decision thresholds, fp32(mean of adjacent
+ *   float64 levels).
+ * wht_block: length B of the blockwise Walsh-Hadamard transform, the largest
+ *   power of two dividing head_dim (128 -> 128, 96 -> 32, 64 -> 64).
+ */
+typedef struct {
+  int32_t head_dim;          /* 64 | 96 | 128                                 */
+  int32_t key_quant_bits;    /* 3 | 4 = Lloyd-Max MSE keys; 8 = FP8 keys      */
+  int32_t value_quant_bits;  /* 3 | 4                                         */
+  int32_t norm_correction;   /* 0 | 1                                         */
+  int64_t seed;              /* base seed (default 42)                        */
+  int32_t key_fp8;           /* key_quant_bits == 8                           */
+  int32_t mse_bits;          /* key bits, or value bits in FP8 mode           */
+  int32_t key_mse_bits;      /* 0 in FP8 mode                                 */
+  int32_t centroid_bits;     /* == mse_bits                                   */
+  int32_t n_centroids;       /* 2^mse_bits                                    */
+  int32_t key_packed_size;   /* bytes                                         */
+  int32_t value_packed_size; /* bytes                                         */
+  int32_t slot_size;         /* key_packed_size + value_packed_size           */
+  int32_t slot_size_aligned; /* slot_size rounded up to even                  */
+  int32_t wht_block;
+  float centroids[16];
+  float midpoints[15];
+} tq_config;
+
+/* Dataclass constructor ([API] TurboQuantConfig fields). head_dim must be 64,
+ * 96 or 128; key_bits 3, 4 or 8; value_bits 3 or 4. Host only. */
+tq_status tq_config_init(int head_dim, int key_bits, int value_bits, int norm_correction,
+                         int64_t seed, tq_config *out);
+
+/* Named preset ([API] from_cache_dtype): turboquant_k8v4 (FP8 keys, 4-bit
+ * values), turboquant_4bit_nc (4/4, norm correction), turboquant_k3v4_nc
+ * (3/4, NC), turboquant_3bit_nc (3/3, NC); seed 42. Unknown names return
+ * TQ_ERR_UNKNOWN_PRESET with the message
+ * "Unknown TurboQuant cache dtype: '<name>'. Valid presets: turboquant_k8v4,
+ * turboquant_4bit_nc, turboquant_k3v4_nc, turboquant_3bit_nc". Host only. */
+tq_status tq_config_from_preset(const char *preset, int head_dim, tq_config *out);
+
+/* Slot bytes per head per position ([API] slot_size / slot_size_aligned):
+ * aligned != 0 gives slot_size_aligned. Returns < 0 on a null or invalid
+ * config. Host only. */
+int32_t tq_slot_size(const tq_config *cfg, int aligned);
+
+/* Bytes of one paged block: block_size * num_kv_heads * slot_size_aligned
+ * ([PR] TurboQuant page size). Returns < 0 on invalid input. Host only. */
+int64_t tq_page_size(const tq_config *cfg, int num_kv_heads, int block_size);
+
+/* The layer's random signs as floats (+1/-1), head_dim of them, for layer
+ * seed = seed + 1337 * layer_idx ([API] seed argument), drawn from
+ * SplitMix64: sign j is -1 when bit 63 of output j is set. Host only; for
+ * checking and for callers that rotate queries themselves. */
+tq_status tq_layer_signs(const tq_config *cfg, int layer_idx, float *signs_out);
+
+/*
+ * Quantize-and-append ([API] docstring and slot layout; [ART] write path):
+ * encodes K[t, h, :] and V[t, h, :] for t < num_tokens, h < num_kv_heads,
+ * and writes the slot into kv_pool at physical slot slot_mapping[t].
+ *
+ *  k, v          device, dtype in_dtype (F32, BF16 or F16), element (t, h, j)
+ *                at t * token_stride + h * head_dim + j; 16-byte aligned;
+ *                token strides are multiples of 8 elements.
+ *  slot_mapping  device int64 [num_tokens]; -1 skips the token; ids outside
+ *                [0, num_blocks * block_size) are skipped too.
+ *  kv_pool       device uint8, layout in the header comment, 16-byte aligned.
+ *
+ * Keys (MSE mode): vec_norm = fp16(||k||), u = Pi k / ||k|| with
+ * Pi = (1/sqrt(B)) H_B diag(signs), index j = number of midpoints strictly
+ * below u_j. Keys (FP8 mode): E4M3FN, round to nearest even, saturating at
+ * +-448. Values: scale = (max - min) / (2^vb - 1), zero = min, both fp16;
+ * code_j = clamp(rint((v_j - zero') / scale'), 0, 2^vb - 1) using the
+ * stored fp16 scale' and zero'. fp32 with a fixed operation order; the
+ * bytes equal the CPU oracle's bit for bit.
+ */
+tq_status tq_quantize_append(const tq_config *cfg, int layer_idx,
+                             const void *k, const void *v, tq_dtype in_dtype,
+                             int64_t num_tokens, int num_kv_heads,
+                             int64_t k_token_stride, int64_t v_token_stride,
+                             const int64_t *slot_mapping,
+                             uint8_t *kv_pool, int64_t num_blocks, int block_size,
+                             void *stream);
+
+/*
+ * Workspace bytes for tq_decode_attention with the same arguments. The
+ * decode splits each sequence's compressed context into chunks of
+ * split_tokens tokens (0 = library choice; otherwise a positive multiple of
+ * 16), plus one chunk for the ring when ring_cap > 0; the workspace holds one
+ * (max, sum, acc[head_dim]) fp32 partial per (sequence, query head, chunk).
+ * num_splits_out (nullable) receives the number of chunks per sequence.
+ */
+tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, int num_q_heads,
+                                   int max_seq_len, int ring_cap, int split_tokens,
+                                   size_t *bytes_out, int *num_splits_out);
+
+/*
+ * Fused decode attention over the compressed cache ([ART] direction 1, ring
+ * buffer from the write-path section):
+ *
+ *   out[b, g, :] = sum_t softmax_t(scale * q[b, g] . k_t) v_t
+ *
+ * over the sequence's compressed tokens 0..seq_lens[b]-1 (dequantized values
+ * k_hat, v_hat) followed by its ring tokens 0..ring_lens[b]-1 (exact bf16).
+ * Query head g reads KV head g / (num_q_heads / num_kv_heads). For MSE keys
+ * the score is computed as n16 * <Pi q, c_idx> (divided by ||c_idx|| under
+ * norm correction), never forming k_hat; FP8 and ring keys use q itself.
+ * A sequence with no tokens outputs zeros.
+ *
+ *  q             device [batch][num_q_heads][head_dim], dtype q_dtype
+ *                (F32, BF16 or F16), contiguous.
+ *  kv_pool       device, as written by tq_quantize_append; 16-byte aligned.
+ *  block_tables  device int32 [batch][max_blocks_per_seq].
+ *  seq_lens      device int32 [batch], compressed tokens per sequence; must
+ *                be <= max_seq_len (the host hint used to size the splits);
+ *                tokens beyond it are ignored.
+ *  ring_k/ring_v device bf16 [batch][num_kv_heads][ring_cap][head_dim], or
+ *                NULL (then ring_lens is ignored and ring_cap must be 0);
+ *                ring_lens device int32 [batch], clamped to ring_cap.
+ *  softmax_scale <= 0 means 1/sqrt(head_dim).
+ *  out           device fp32 [batch][num_q_heads][head_dim].
+ *  workspace     device, at least tq_decode_workspace_size bytes, 16-byte
+ *                aligned; its contents on entry do not matter.
+ *  block_size    a multiple of 16.
+ */
+tq_status tq_decode_attention(const tq_config *cfg, int layer_idx,
+                              const void *q, tq_dtype q_dtype,
+                              int batch, int num_q_heads, int num_kv_heads,
+                              const uint8_t *kv_pool, int64_t num_blocks, int block_size,
+                              const int32_t *block_tables, int max_blocks_per_seq,
+                              const int32_t *seq_lens, int max_seq_len,
+                              const void *ring_k, const void *ring_v,
+                              const int32_t *ring_lens, int ring_cap,
+                              float softmax_scale, float *out,
+                              void *workspace, size_t workspace_bytes,
+                              int split_tokens, void *stream);
+
+/*
+ * Dequantize slots back to the original basis ([API] docstring: centroids,
+ * re-normalized under norm correction, then the inverse rotation; values
+ * scale' * code + zero'), fp32 with the oracle's fixed operation order:
+ *
+ *  k_out[i, h, :], v_out[i, h, :] for i < n, h < num_kv_heads, from physical
+ *  slot slot_ids[i] (device int64; -1 or out-of-range ids give zeros).
+ *  k_out, v_out: device fp32 [n][num_kv_heads][head_dim].
+ */
+tq_status tq_dequant(const tq_config *cfg, int layer_idx,
+                     const uint8_t *kv_pool, int64_t num_blocks, int num_kv_heads,
+                     int block_size, const int64_t *slot_ids, int64_t n,
+                     float *k_out, float *v_out, void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *tq_last_error(void);
+
+/* Library version string, e.g. "tq-mi355x 0.1.0 gfx950". */
+const char *tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

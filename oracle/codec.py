@@ -175,7 +175,9 @@ def encode_keys_mse(x, cfg: TQConfig, layer_idx: int):
     with np.errstate(divide="ignore"):
         r = np.where(n == 0, np.float32(0), np.float32(1) / p).astype(np.float32)
     u = z * r[:, None]
-    idx = (u[:, :, None] > m32[None, None, :]).sum(axis=2).astype(np.uint8)
+    # index = number of midpoints strictly below u (searchsorted with side
+    # "left" returns exactly that count for an ascending table)
+    idx = np.searchsorted(m32, u, side="left").astype(np.uint8)
     return idx, norm16
 
 

@@ -1,0 +1,142 @@
+"""CPU tests of the C-ABI library: it loads without a GPU, exports every symbol
+include/tq.h declares, its host-side config arithmetic and tables equal the
+oracle's bit for bit, and argument errors are reported before anything is
+launched. No GPU work is enqueued here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import config as OC
+from oracle import lloyd_max as OL
+from oracle import rotation as OR
+from tests.conftest import ROOT
+
+tq = pytest.importorskip("compressed_decode_attention_quantize_amd",
+                         reason="libtq.so not built (run __graft_entry__.build())")
+
+
+def test_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "tq.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(tq_[a-z_0-9]+)\s*\(", header, re.M))
+    assert {"tq_config_init", "tq_quantize_append", "tq_decode_attention", "tq_dequant"} <= declared
+    for name in declared:
+        assert hasattr(tq.lib(), name), name
+    assert set(tq.EXPORTED) == declared
+
+
+PRESETS = ["turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"]
+
+
+@pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_preset_config_matches_oracle(preset, d):
+    c = tq.config_from_preset(preset, d)
+    o = OC.from_cache_dtype(preset, d)
+    for f in ("head_dim", "key_quant_bits", "value_quant_bits", "seed", "key_packed_size",
+              "value_packed_size", "slot_size", "slot_size_aligned", "mse_bits", "key_mse_bits",
+              "centroid_bits", "n_centroids", "wht_block"):
+        assert getattr(c, f) == int(getattr(o, f)), f
+    assert bool(c.norm_correction) == o.norm_correction and bool(c.key_fp8) == o.key_fp8
+    assert tq.slot_size(c) == o.slot_size_aligned and tq.slot_size(c, aligned=False) == o.slot_size
+    assert tq.page_size(c, 8, 16) == 16 * 8 * o.slot_size_aligned
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("bits", [3, 4])
+def test_tables_bit_equal_to_oracle(d, bits):
+    c = tq.config_init(d, bits, 4, False, 42)
+    c32, m32 = OL.tables_f32(d, bits)
+    got_c = np.array(list(c.centroids), np.float32)[: 2 ** bits]
+    got_m = np.array(list(c.midpoints), np.float32)[: 2 ** bits - 1]
+    assert np.array_equal(got_c.view(np.uint32), c32.view(np.uint32))
+    assert np.array_equal(got_m.view(np.uint32), m32.view(np.uint32))
+
+
+@pytest.mark.parametrize("seed,layer", [(42, 0), (42, 7), (0, 3), (2 ** 40 + 5, 1)])
+def test_layer_signs_equal_oracle(seed, layer):
+    c = tq.config_init(128, 3, 4, True, seed)
+    assert np.array_equal(tq.layer_signs(c, layer), OR.signs(seed, layer, 128))
+
+
+def test_unknown_preset_error_text():
+    with pytest.raises(tq.TQError) as ei:
+        tq.config_from_preset("turboquant_2bit", 128)
+    assert ei.value.status == 2
+    assert ei.value.message == ("Unknown TurboQuant cache dtype: 'turboquant_2bit'. Valid presets: "
+                                "turboquant_k8v4, turboquant_4bit_nc, turboquant_k3v4_nc, turboquant_3bit_nc")
+
+
+@pytest.mark.parametrize("args,status", [((100, 3, 4), 3), ((128, 5, 4), 1), ((128, 3, 2), 1), ((256, 3, 4), 3)])
+def test_config_init_rejects(args, status):
+    with pytest.raises(tq.TQError) as ei:
+        tq.config_init(*args)
+    assert ei.value.status == status
+
+
+def _c_call(name, *args):
+    return getattr(tq.lib(), name)(*args)
+
+
+def test_quantize_argument_errors_before_launch():
+    c = tq.config_from_preset("turboquant_4bit_nc", 128)
+    buf = ctypes.create_string_buffer(4096 + 16)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    cfgp = ctypes.byref(c)
+    # NULL k
+    assert _c_call("tq_quantize_append", cfgp, 0, None, al, 1, 4, 8, 1024, 1024, al, al, 10, 16, None) == 1
+    # misaligned pool
+    assert _c_call("tq_quantize_append", cfgp, 0, al, al, 1, 4, 8, 1024, 1024, al, al + 2, 10, 16, None) == 1
+    # token stride too small
+    assert _c_call("tq_quantize_append", cfgp, 0, al, al, 1, 4, 8, 512, 1024, al, al, 10, 16, None) == 1
+    # bad dtype
+    assert _c_call("tq_quantize_append", cfgp, 0, al, al, 7, 4, 8, 1024, 1024, al, al, 10, 16, None) == 1
+    assert "dtype" in tq.last_error()
+    # zero tokens is a no-op success even with NULL pointers
+    assert _c_call("tq_quantize_append", cfgp, 0, None, None, 1, 0, 8, 1024, 1024, None, None, 10, 16, None) == 0
+    # a modified config is rejected
+    bad = tq.config_from_preset("turboquant_4bit_nc", 128)
+    bad.slot_size_aligned = 100
+    assert _c_call("tq_quantize_append", ctypes.byref(bad), 0, al, al, 1, 4, 8, 1024, 1024, al, al, 10, 16, None) == 1
+
+
+def _decode(c, **kw):
+    buf = ctypes.create_string_buffer(1 << 16)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    a = dict(q=al, qd=1, batch=2, hq=8, hkv=2, pool=al, nblocks=4, bs=16, tables=al, maxb=2, lens=al,
+             maxlen=32, rk=None, rv=None, rl=None, rcap=0, scale=0.0, out=al, ws=al, wsb=1 << 15, split=0)
+    a.update(kw)
+    return _c_call("tq_decode_attention", ctypes.byref(c), 0, a["q"], a["qd"], a["batch"], a["hq"], a["hkv"],
+                   a["pool"], a["nblocks"], a["bs"], a["tables"], a["maxb"], a["lens"], a["maxlen"], a["rk"],
+                   a["rv"], a["rl"], a["rcap"], ctypes.c_float(a["scale"]), a["out"], a["ws"],
+                   ctypes.c_size_t(a["wsb"]), a["split"], None)
+
+
+def test_decode_argument_errors_before_launch():
+    c = tq.config_from_preset("turboquant_3bit_nc", 128)
+    assert _decode(c, hq=7) == 1                       # Hq not a multiple of Hkv
+    assert _decode(c, hq=64, hkv=2) == 3               # more than 16 q heads per kv head
+    assert _decode(c, bs=8) == 3                       # block size not a multiple of 16
+    assert _decode(c, wsb=8) == 4 and "workspace" in tq.last_error()
+    assert _decode(c, ws=None) == 4
+    assert _decode(c, rcap=128) == 1                   # ring_cap without ring tensors
+    assert _decode(c, rk=1024, rv=None) == 1           # half a ring
+    assert _decode(c, split=24) == 1                   # split not a multiple of 16
+    assert _decode(c, q=None) == 1
+    assert _decode(c, batch=0) == 0                    # nothing to do
+
+
+def test_workspace_size_and_plan():
+    c = tq.config_from_preset("turboquant_k8v4", 128)
+    b, n = tq.decode_workspace_size(c, 16, 32, 8192, 0, 256)
+    assert n == 32 and b == 16 * 32 * 32 * 130 * 4
+    b, n = tq.decode_workspace_size(c, 16, 32, 8192, 128, 256)
+    assert n == 33
+    b, n = tq.decode_workspace_size(c, 4, 8, 0, 0, 0)
+    assert n == 1 and b == 4 * 8 * 1 * 130 * 4
+    _, n_auto = tq.decode_workspace_size(c, 16, 32, 8192)
+    assert n_auto >= 1
