@@ -31,7 +31,26 @@ if not os.path.exists(LIB_PATH):
         f"libtq.so not found at {LIB_PATH}; build it with "
         "`python compressed_decode_attention_quantize_amd/csrc/build.py`")
 
+# torch ships its own HIP runtime (libamdhip64, same soname as ROCm's). It must
+# be the one libtq binds to: load torch first so the dynamic linker resolves
+# libtq's libamdhip64.so.7 to the already-loaded copy. Two runtimes in one
+# process do not share the device ("no ROCm-capable device is detected").
+import torch as _torch_for_hip_runtime  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_loaded() -> list:
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes_loaded()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process: " + ", ".join(_hip_runtimes_loaded()) +
+                      "; import torch before any other HIP library")
 
 TQ_OK = 0
 STATUS_NAMES = {0: "TQ_OK", 1: "TQ_ERR_INVALID_ARG", 2: "TQ_ERR_UNKNOWN_PRESET",

@@ -274,6 +274,8 @@ def append(pool, k, v, slot_mapping, cfg: TQConfig, layer_idx: int) -> None:
     k = np.asarray(k, dtype=np.float32)
     v = np.asarray(v, dtype=np.float32)
     t, h, d = k.shape
+    if t == 0:
+        return
     slots = encode_slots(k.reshape(t * h, d), v.reshape(t * h, d), cfg, layer_idx)
     write_pool(pool, slots.reshape(t, h, -1), slot_mapping)
 
