@@ -74,6 +74,7 @@ class Config(ctypes.Structure):
         ("value_packed_size", ctypes.c_int32), ("slot_size", ctypes.c_int32),
         ("slot_size_aligned", ctypes.c_int32), ("wht_block", ctypes.c_int32),
         ("centroids", ctypes.c_float * 16), ("midpoints", ctypes.c_float * 15),
+        ("centroid_scale", ctypes.c_float),
     ]
 
     def __repr__(self):

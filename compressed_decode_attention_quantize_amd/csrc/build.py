@@ -29,7 +29,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=of
           "-Wall", "-Wno-unused-function"]
 # Device code: gfx950 only; packed fp32 arithmetic is disabled on purpose.
 DEVICE = ["-x", "hip", "--offload-arch=gfx950",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in VGPRs: the online softmax rescales them with
+          # VALU ops, which cannot read AGPRs
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:

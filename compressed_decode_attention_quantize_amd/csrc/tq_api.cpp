@@ -156,6 +156,7 @@ TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, con
   const float scale = softmax_scale > 0.0f ? softmax_scale
                                            : static_cast<float>(1.0 / std::sqrt(static_cast<double>(cfg->head_dim)));
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.centroid_scale = cfg->centroid_scale;
   layer_sign_mask(*cfg, layer_idx, p.sign_words);
   for (int i = 0; i < 16; ++i) p.centroids[i] = cfg->centroids[i];
   const int err = launch_decode(*cfg, q_dtype, p, stream);

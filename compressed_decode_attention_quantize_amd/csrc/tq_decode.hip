@@ -1,18 +1,35 @@
-// Fused decode attention over compressed slots: split kernel + reduce kernel.
+// Fused decode attention over compressed slots.
 //
 // Source: hnwysp.cn article on the stand-alone turboquant project,
 // next-directions section, direction 1 (one pass over the compressed data,
-// flash-attention style online softmax block by block, query rotated forward
-// so the D-dim keys are never rotated back, no materialised FP16 KV); the
-// write-path section (128-token bf16 exact ring buffer) for the ring chunk;
-// vLLM API page TurboQuantConfig docstring for norm correction.
+// flash-attention style online softmax block by block, the query rotated
+// forward so D-dim keys are never rotated back, no materialised FP16 KV);
+// its write-path section (128-token bf16 exact ring buffer) for the ring
+// chunk; vLLM API page TurboQuantConfig docstring for norm correction.
 //
-// Work split (flash-decoding): one workgroup per (split, kv head, sequence).
-// A split is a range of split_tokens compressed positions, or the ring. It
-// walks 16-token tiles; since block_size is a multiple of 16 each tile's 16
-// slots are contiguous in the pool ([blk][h][bs][S]). It writes an
-// unnormalised partial (m, l, acc[D]) in the exp2 domain; the reduce kernel
-// merges the partials of a (sequence, query head) by log-sum-exp.
+// Three kernels on one stream:
+//
+//  split kernel  (compressed tokens; one wave per (sequence, KV head, split),
+//                four waves per workgroup sharing a code->f16 pair table)
+//     per 16-token tile, staged HBM -> LDS with 16-byte loads one tile ahead:
+//       K~ = centroid values (MSE: pair-table lookup, FP8: hardware cvt), f16
+//       S^T[t][g] = K~ . (Pi q)^T           MFMA 16x16x32 f16, D/32 of them
+//       |c_t|^2   = diag(K~ K~^T)            (norm correction only)
+//       s = S^T * n16_t * scale*log2(e) (/|c_t|), online softmax in exp2,
+//       the running max only ever grows, acc is rescaled when it does
+//       Out^T[j][g] += (code_tj - c0)^T . (p_t s'_t)   MFMA 16x16x16 f16,
+//                      codes expanded by the 0x6400 exponent trick in place,
+//                      the weights p_t s'_t as f16 hi + lo parts
+//       zero terms  += p_t (z'_t + c0 s'_t)   fp32
+//     writes an unnormalised partial (m, l, acc[D]) per (sequence, q head).
+//  ring kernel   (exact bf16 ring tokens, fp32 VALU; one workgroup per
+//                (sequence, KV head)), same partial format.
+//  reduce kernel (log-sum-exp merge of a (sequence, q head)'s partials).
+//
+// MFMA operand layouts used (gfx950, wave64), checked on hardware:
+//  16x16x32 f16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], e<8;
+//  16x16x16 f16: lane l holds A[l%16][4(l/16)+e], B[4(l/16)+e][l%16], e<4;
+//  both: result lane l register r = D[4(l/16)+r][l%16].
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -20,159 +37,544 @@
 namespace tq {
 namespace {
 
-constexpr int kDecThreads = 256;
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 constexpr int kTile = 16;
-constexpr int kMaxG = 16;
-constexpr int kMaxSlot = 196;
+constexpr int kWaves = 4;               // waves (= splits) per workgroup
+constexpr int kPartStride_pad = 4;      // partial = [m, l, -, -, acc[D]]
+
+__device__ __forceinline__ int partial_stride(int d) { return d + kPartStride_pad; }
+
+// Compile-time geometry of one (head_dim, key bits, value bits) variant.
+template <int D, int KB, int VB>
+struct Geo {
+  static constexpr bool kMse = KB != 8;
+  static constexpr int kKeyCodeBytes = kMse ? D * KB / 8 : D;
+  static constexpr int kKeyBytes = kMse ? kKeyCodeBytes + 2 : D;
+  static constexpr int kValCodeBytes = D * VB / 8;
+  static constexpr int kSlot = kKeyBytes + kValCodeBytes + 4;   // even for D % 32 == 0
+  static constexpr int kKM = D / 32;                // score MFMAs per tile
+  static constexpr int kLaneKeyBytes = kKeyCodeBytes / 4;       // key bytes per lane
+  static constexpr int kGroups = D / 8;             // 8-element value groups
+  static constexpr int kTileBytes = kTile * kSlot;
+  static constexpr int kTileChunks = kTileBytes / 16;           // 16-byte chunks
+  static constexpr int kChunksPerLane = (kTileChunks + 63) / 64;
+  static constexpr int kQBytes = 2 * 16 * D * 2;    // f16 rotated queries, hi and lo [2][16][D]
+  // one wave's LDS: the staged tile or the rotated queries, plus slack for
+  // the funnel-shifted reads that run up to 7 bytes past a field
+  static constexpr int kScratch = (kTileBytes > kQBytes ? kTileBytes : kQBytes) + 16;
+  static constexpr int kLut = KB == 4 ? 256 : (KB == 3 ? 64 : 1);
+  static_assert(kSlot % 2 == 0, "slot size must be even");
+};
+
+template <int N>
+struct Words {
+  uint32_t w[N];
+};
+
+// NB bytes at byte offset `off` (any alignment) of an LDS word array, as
+// NB/4 (rounded up) little-endian words: aligned dword reads and a byte
+// funnel shift. Offsets, not pointer casts, keep the accesses in the LDS
+// address space.
+template <int NB>
+__device__ __forceinline__ Words<(NB + 3) / 4> lds_bytes(const uint32_t *words, uint32_t off) {
+  constexpr int NW = (NB + 3) / 4;
+  const uint32_t w0 = off >> 2;
+  const uint32_t sh = off & 3u;
+  uint32_t raw[NW + 1];
+#pragma unroll
+  for (int i = 0; i <= NW; ++i) raw[i] = words[w0 + i];
+  Words<NW> out;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) out.w[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
+  return out;
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, uint32_t b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 x = __builtin_bit_cast(h2, a), y = __builtin_bit_cast(h2, b);
+  return __builtin_bit_cast(uint32_t, x + y);
+}
+
+__device__ __forceinline__ uint32_t f16_pair_bits(float lo, float hi) {
+  return float_to_f16_bits(lo) | (float_to_f16_bits(hi) << 16);
+}
+
+// Exponent-trick expansion of value codes of one element for a pair of
+// tokens: `x` holds the two tokens' code bits in its low and high halves,
+// `mask` selects the element's field in place (bits <= 9), so
+// (x & mask) | 0x6400 is the f16 1024 + code * 2^pos in each half; adding
+// -(1024 + 2^pos * c0) leaves 2^pos * (code - c0), exact in f16.
+__device__ __forceinline__ uint32_t code_pair(uint32_t x, uint32_t mask, uint32_t neg_off) {
+  // one v_and_or_b32 (the exponent constant sits in a VGPR: gfx950 VOP3
+  // encodings take no literal operand)
+  uint32_t r;
+  const uint32_t magic = 0x64006400u;
+  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
+  return pk_add_f16(r, neg_off);
+}
+
+// Value codes of element group i (8 elements) for tokens 4kq..4kq+3 as the
+// A operands of the eight value MFMAs (element 8i+c in MFMA c), with the
+// per-element power-of-two scales the expansion leaves (inv_scale[c]).
+template <int VB>
+struct ValueExpand;
+
+template <>
+struct ValueExpand<4> {
+  static constexpr int kC0 = 8;
+  __device__ static void run(const uint32_t d[4], half4_t av[8]) {
+    // d[r]: 8 nibbles (elements 8i..8i+7) of token 4kq + r
+    const uint32_t off_even = f16_pair_bits(-(1024.0f + kC0), -(1024.0f + kC0));
+    const uint32_t off_odd = f16_pair_bits(-(1024.0f + 16.0f * kC0), -(1024.0f + 16.0f * kC0));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t sel = static_cast<uint32_t>(k) | (0x0Cu << 8) | ((4u + k) << 16) | (0x0Cu << 24);
+      const uint32_t x01 = perm(d[1], d[0], sel);
+      const uint32_t x23 = perm(d[3], d[2], sel);
+      u32x2_t e, o;
+      e[0] = code_pair(x01, 0x000F000Fu, off_even);
+      e[1] = code_pair(x23, 0x000F000Fu, off_even);
+      o[0] = code_pair(x01, 0x00F000F0u, off_odd);
+      o[1] = code_pair(x23, 0x00F000F0u, off_odd);
+      av[2 * k] = __builtin_bit_cast(half4_t, e);
+      av[2 * k + 1] = __builtin_bit_cast(half4_t, o);
+    }
+  }
+  __device__ static float inv_scale(int c) { return (c & 1) ? (1.0f / 16.0f) : 1.0f; }
+};
+
+template <>
+struct ValueExpand<3> {
+  static constexpr int kC0 = 4;
+  // element c sits at bits 3c..3c+2; after the byte selection below its
+  // field starts at bit kPos[c] of a 16-bit half.
+  __device__ static constexpr int pos(int c) {
+    return c == 0 ? 0 : c == 1 ? 3 : c == 2 ? 6 : c == 3 ? 1 : c == 4 ? 4 : c == 5 ? 7 : c == 6 ? 2 : 5;
+  }
+  __device__ static void run(const uint32_t d[4], half4_t av[8]) {
+    // d[r]: 24 bits (elements 8i..8i+7) of token 4kq + r
+    constexpr uint32_t selX = 0u | (1u << 8) | (4u << 16) | (5u << 24);     // bits 0..15
+    constexpr uint32_t selY = 1u | (2u << 8) | (5u << 16) | (6u << 24);     // bits 8..23
+    constexpr uint32_t selZ = 2u | (0x0Cu << 8) | (6u << 16) | (0x0Cu << 24);  // bits 16..23
+    uint32_t xs[3][2];
+    xs[0][0] = perm(d[1], d[0], selX);
+    xs[0][1] = perm(d[3], d[2], selX);
+    xs[1][0] = perm(d[1], d[0], selY);
+    xs[1][1] = perm(d[3], d[2], selY);
+    xs[2][0] = perm(d[1], d[0], selZ);
+    xs[2][1] = perm(d[3], d[2], selZ);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int src = c < 3 ? 0 : (c < 6 ? 1 : 2);
+      const uint32_t m16 = 7u << pos(c);
+      const uint32_t mask = m16 | (m16 << 16);
+      const float off = -(1024.0f + static_cast<float>(1 << pos(c)) * kC0);
+      const uint32_t neg = f16_pair_bits(off, off);
+      u32x2_t v;
+      v[0] = code_pair(xs[src][0], mask, neg);
+      v[1] = code_pair(xs[src][1], mask, neg);
+      av[c] = __builtin_bit_cast(half4_t, v);
+    }
+  }
+  __device__ static float inv_scale(int c) { return 1.0f / static_cast<float>(1 << pos(c)); }
+};
+
+// Key operand of one lane: token t = lane % 16, elements kq*D/4 .. +D/4-1 as
+// f16 centroid values (MSE, via the pair table) or FP8-decoded values.
+template <int D, int KB>
+__device__ __forceinline__ void key_operand(const uint32_t *words, uint32_t off, const uint32_t *lut,
+                                            half8_t kf[D / 32]) {
+  using G = Geo<D, KB, 4>;
+  constexpr int LB = G::kLaneKeyBytes;
+  const auto kw = lds_bytes<LB>(words, off);
+  if constexpr (KB == 4) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      const uint32_t w = kw.w[m];
+      u32x4_t v;
+      v[0] = lut[w & 0xffu];
+      v[1] = lut[(w >> 8) & 0xffu];
+      v[2] = lut[(w >> 16) & 0xffu];
+      v[3] = lut[w >> 24];
+      kf[m] = __builtin_bit_cast(half8_t, v);
+    }
+  } else if constexpr (KB == 3) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      // 24 bits of elements 8m..8m+7 start at bit 24m of the lane's bytes
+      const int bit = 24 * m;
+      const int wi = bit >> 5, sh = bit & 31;
+      uint32_t g = kw.w[wi] >> sh;
+      if (sh > 8) g |= kw.w[wi + 1] << (32 - sh);
+      u32x4_t v;
+      v[0] = lut[g & 63u];
+      v[1] = lut[(g >> 6) & 63u];
+      v[2] = lut[(g >> 12) & 63u];
+      v[3] = lut[(g >> 18) & 63u];
+      kf[m] = __builtin_bit_cast(half8_t, v);
+    }
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      const uint32_t a = kw.w[2 * m], b = kw.w[2 * m + 1];
+      u32x4_t v;
+      v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false));
+      v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true));
+      v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false));
+      v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true));
+      kf[m] = __builtin_bit_cast(half8_t, v);
+    }
+  }
+}
+
+// 16-bit field at an even byte offset of an LDS word array.
+__device__ __forceinline__ uint32_t lds_u16(const uint32_t *words, uint32_t off) {
+  const uint32_t w = words[off >> 2];
+  return (off & 2u) ? (w >> 16) : (w & 0xffffu);
+}
 
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams p, int q_dtype) {
-  constexpr int kGroups = kDecThreads / D;         // thread groups over query heads
-  constexpr int kAccPerThread = (kMaxG + kGroups - 1) / kGroups;
-  constexpr bool kMse = KB != 8;
-  constexpr int kKeyIdxBytes = kMse ? (D * KB) / 8 : D;
-  constexpr int kValCodeBytes = (D * VB) / 8;
+__global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeParams p, int q_dtype) {
+  using GE = Geo<D, KB, VB>;
+  using VX = ValueExpand<VB>;
+  constexpr int S = GE::kSlot;
+  constexpr int KM = GE::kKM;
 
+  __shared__ uint32_t lut[GE::kLut];
+  __shared__ __align__(16) uint32_t scratch[kWaves][GE::kScratch / 4];
+  __shared__ __align__(16) float tok[kWaves][3][16];
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int kq = lane >> 4;
+
+  if constexpr (GE::kMse) {
+    for (int e = threadIdx.x; e < GE::kLut; e += 64 * kWaves) {
+      const int lo = e & ((1 << KB) - 1), hi = e >> KB;
+      lut[e] = f16_pair_bits(p.centroids[lo] * p.centroid_scale, p.centroids[hi] * p.centroid_scale);
+    }
+  }
+  __syncthreads();  // the only workgroup barrier; waves are independent below
+
+  // the wave index is uniform across the wave: say so, so that the split
+  // bookkeeping, block-table reads and tile addresses stay in scalar registers
+  const int split = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(wave);
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  if (split >= p.num_splits) return;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  int len = p.seq_lens[b];
+  len = min(max(len, 0), min(p.max_seq_len, p.max_blocks_per_seq * p.block_size));
+  const int begin = split * p.split_tokens;
+  const int end = min(len, begin + p.split_tokens);
+  const int pstride = partial_stride(D);
+  float *part_base = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + h * G) * p.splits_total * pstride +
+                     static_cast<int64_t>(split) * pstride;
+
+  if (begin >= end) {
+    // empty split: identity partial
+    if (lane < G) {
+      float *dst = part_base + static_cast<int64_t>(lane) * p.splits_total * pstride;
+      dst[0] = -INFINITY;
+      dst[1] = 0.0f;
+    }
+    return;
+  }
+
+  uint32_t *scr = scratch[wave];  // this wave's LDS: queries, then the staged tile
+
+  // ---- rotated queries (f16) -> LDS [16][D], then into MFMA B operands
+  {
+    using T = Team<D>;
+    const int team = lane / T::kLanes;
+    const int r = lane - team * T::kLanes;
+    const int rows_per_pass = T::kPerWave;
+    _Float16 *qs = reinterpret_cast<_Float16 *>(scr);
+    for (int g0 = 0; g0 < 16; g0 += rows_per_pass) {
+      const int g = g0 + team;
+      float x[8];
+      const bool live = team < rows_per_pass && g < G;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        x[i] = live ? load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + 8 * r + i)
+                    : 0.0f;
+      if constexpr (GE::kMse) {
+        const uint32_t sb = lane_sign_bits(p.sign_words, r);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = flip_sign(x[i], (sb >> i) & 1u);
+        team_wht<D>(x, r % T::kBlockLanes);
+        const float rb = rsqrtf(static_cast<float>(T::kBlock));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] *= rb;
+      }
+      if (team < rows_per_pass && g < 16) {
+        u32x4_t v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = f16_pair_bits(x[2 * i], x[2 * i + 1]);
+        *reinterpret_cast<u32x4_t *>(qs + g * D + 8 * r) = v;
+        // the low parts go to the second half of the scratch
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float h0 = f16_bits_to_float(v[i] & 0xffffu), h1 = f16_bits_to_float(v[i] >> 16);
+          v[i] = f16_pair_bits(x[2 * i] - h0, x[2 * i + 1] - h1);
+        }
+        *reinterpret_cast<u32x4_t *>(qs + 16 * D + g * D + 8 * r) = v;
+      }
+    }
+  }
+  half8_t qf[KM], ql[KM];  // rotated queries as f16 hi + lo parts
+  {
+    const _Float16 *qs = reinterpret_cast<const _Float16 *>(scr);
+#pragma unroll
+    for (int m = 0; m < KM; ++m)
+      qf[m] = *reinterpret_cast<const half8_t *>(qs + col * D + kq * (D / 4) + 8 * m);
+#pragma unroll
+    for (int m = 0; m < KM; ++m)
+      ql[m] = *reinterpret_cast<const half8_t *>(qs + 16 * D + col * D + kq * (D / 4) + 8 * m);
+  }
+
+  // ---- tile loop
+  float4_t acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_lane = 0.0f, z_lane = 0.0f;
+
+  u32x4_t pre[GE::kChunksPerLane];
+  bool pre_ok = false;
+  auto issue = [&](int tile0) {
+    const int lblk = tile0 / p.block_size;
+    const int off = tile0 - lblk * p.block_size;
+    const int phys = p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + lblk];
+    pre_ok = phys >= 0 && phys < p.num_blocks;
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+        p.pool + ((static_cast<int64_t>(pre_ok ? phys : 0) * p.num_kv_heads + h) * p.block_size + off) *
+                     static_cast<int64_t>(S));
+#pragma unroll
+    for (int k = 0; k < GE::kChunksPerLane; ++k) {
+      const int c = lane + 64 * k;
+      pre[k] = (pre_ok && c < GE::kTileChunks) ? src[c] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  issue(begin);
+
+  const float c0 = static_cast<float>(VX::kC0);
+  const float inv_sigma = 1.0f / p.centroid_scale;
+  for (int tile0 = begin; tile0 < end; tile0 += kTile) {
+    const int ntok = min(kTile, end - tile0);
+    const bool tile_ok = pre_ok;
+#pragma unroll
+    for (int k = 0; k < GE::kChunksPerLane; ++k) {
+      const int c = lane + 64 * k;
+      if (c < GE::kTileChunks) reinterpret_cast<u32x4_t *>(scr)[c] = pre[k];
+    }
+    if (tile0 + kTile < end) issue(tile0 + kTile);
+
+    // per-token scalars: lane t < 16 reads its slot's norm / scale / zero
+    if (lane < 16) {
+      const uint32_t slot = static_cast<uint32_t>(lane * S);
+      const bool ok = tile_ok && lane < ntok;
+      float fb = p.scale_log2;
+      if constexpr (GE::kMse) fb *= f16_bits_to_float(lds_u16(scr, slot + GE::kKeyCodeBytes));
+      const float s1 = f16_bits_to_float(lds_u16(scr, slot + GE::kKeyBytes + GE::kValCodeBytes));
+      const float z1 = f16_bits_to_float(lds_u16(scr, slot + GE::kKeyBytes + GE::kValCodeBytes + 2));
+      tok[wave][0][lane] = ok ? fb : -1.0f;  // negative marks a masked token
+      tok[wave][1][lane] = ok ? s1 : 0.0f;
+      tok[wave][2][lane] = ok ? fmaf(c0, s1, z1) : 0.0f;
+    }
+
+    // keys -> scores S^T[4kq + r][col]
+    half8_t kf[KM];
+    key_operand<D, KB>(scr, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
+    float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[m], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], ql[m], sc, 0, 0, 0);
+    }
+    float4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (GE::kMse) {
+      if (p.norm_correction) {
+#pragma unroll
+        for (int m = 0; m < KM; ++m) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], kf[m], gram, 0, 0, 0);
+      }
+    }
+
+    // value codes of element group col for tokens 4kq..4kq+3
+    half4_t av[8];
+    {
+      uint32_t d[4];
+      if (col < GE::kGroups) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const auto w = lds_bytes<VB>(scr, static_cast<uint32_t>((4 * kq + r) * S + GE::kKeyBytes + VB * col));
+          d[r] = w.w[0];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[r] = 0u;
+      }
+      VX::run(d, av);  // rows col >= kGroups are padding and never written out
+    }
+
+    const float4_t fb4 = *reinterpret_cast<const float4_t *>(&tok[wave][0][4 * kq]);
+    const float4_t s14 = *reinterpret_cast<const float4_t *>(&tok[wave][1][4 * kq]);
+    const float4_t zc4 = *reinterpret_cast<const float4_t *>(&tok[wave][2][4 * kq]);
+
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float f = fb4[r];
+      if constexpr (GE::kMse) {
+        // centroids carry the table scale sigma: it cancels under norm
+        // correction and is divided out otherwise
+        if (p.norm_correction) {
+          const float nn = __shfl(gram[r], 20 * kq + r, 64);
+          f = f * rsqrtf(nn);
+        } else {
+          f = f * inv_sigma;
+        }
+      }
+      s[r] = (fb4[r] >= 0.0f) ? sc[r] * f : -INFINITY;
+    }
+    // running max over the tile: 4 registers, then the 4 lane groups
+    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    if (mt > m_run) {
+      const float alpha = exp2f(m_run - mt);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+      l_lane *= alpha;
+      z_lane *= alpha;
+      m_run = mt;
+    }
+    const float mr = (m_run == -INFINITY) ? 0.0f : m_run;
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = __builtin_amdgcn_exp2f(s[r] - mr);
+      l_lane += pr[r];
+      z_lane = fmaf(pr[r], zc4[r], z_lane);
+    }
+    // weights p * s' as f16 hi + lo parts: the value contraction then sees
+    // them to ~22 bits (f16 alone leaves a 2^-12 error that cancellation in
+    // the weighted sum can amplify)
+    float w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = pr[r] * s14[r];
+    u32x2_t hw, lw;
+    hw[0] = f16_pair_bits(w[0], w[1]);
+    hw[1] = f16_pair_bits(w[2], w[3]);
+    lw[0] = f16_pair_bits(w[0] - f16_bits_to_float(hw[0] & 0xffffu), w[1] - f16_bits_to_float(hw[0] >> 16));
+    lw[1] = f16_pair_bits(w[2] - f16_bits_to_float(hw[1] & 0xffffu), w[3] - f16_bits_to_float(hw[1] >> 16));
+    const half4_t pvh = __builtin_bit_cast(half4_t, hw);
+    const half4_t pvl = __builtin_bit_cast(half4_t, lw);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[c], pvh, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[c], pvl, acc[c], 0, 0, 0);
+    }
+  }
+
+  // ---- partial (m, l, acc + zero terms) of query head col
+  l_lane += __shfl_xor(l_lane, 16, 64);
+  l_lane += __shfl_xor(l_lane, 32, 64);
+  z_lane += __shfl_xor(z_lane, 16, 64);
+  z_lane += __shfl_xor(z_lane, 32, 64);
+  if (col < G) {
+    float *dst = part_base + static_cast<int64_t>(col) * p.splits_total * pstride;
+    if (kq == 0) {
+      dst[0] = m_run;
+      dst[1] = l_lane;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int grp = 4 * kq + r;
+      if (grp < GE::kGroups) {
+        float4_t lo, hi;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          lo[c] = fmaf(acc[c][r], VX::inv_scale(c), z_lane);
+          hi[c] = fmaf(acc[c + 4][r], VX::inv_scale(c + 4), z_lane);
+        }
+        *reinterpret_cast<float4_t *>(dst + 4 + 8 * grp) = lo;
+        *reinterpret_cast<float4_t *>(dst + 4 + 8 * grp + 4) = hi;
+      }
+    }
+  }
+}
+
+// Exact bf16 ring tokens (and the empty-context partial): fp32 VALU, one
+// workgroup per (sequence, KV head), partial index p.num_splits.
+constexpr int kRingThreads = 256;
+constexpr int kMaxG = 16;
+
+template <int D>
+__global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams p, int q_dtype) {
+  constexpr int kGroups = kRingThreads / D;
+  constexpr int kAccPerThread = (kMaxG + kGroups - 1) / kGroups;
   __shared__ float q_s[kMaxG][D];
   __shared__ float k_s[kTile][D + 1];
   __shared__ float v_s[kTile][D + 1];
-  __shared__ float f_s[kTile];
   __shared__ float p_s[kMaxG][kTile];
   __shared__ float alpha_s[kMaxG];
-  __shared__ float cent_s[16];
-  __shared__ __align__(16) uint8_t run_s[kTile * kMaxSlot];
 
-  const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int G = p.num_q_heads / p.num_kv_heads;
-  const bool ring_split = split >= p.num_splits;
+  const int split = p.num_splits;
+  const int end = (p.ring_k != nullptr) ? min(max(p.ring_lens[b], 0), p.ring_cap) : 0;
 
-  // ---- token range of this split
-  int begin = 0, end = 0;
-  if (!ring_split) {
-    int len = p.seq_lens[b];
-    len = min(max(len, 0), min(p.max_seq_len, p.max_blocks_per_seq * p.block_size));
-    begin = split * p.split_tokens;
-    end = min(len, begin + p.split_tokens);
-  } else if (p.ring_k != nullptr) {
-    end = min(max(p.ring_lens[b], 0), p.ring_cap);
-  }
-
-  if (tid < 16) cent_s[tid] = p.centroids[tid];
-
-  // ---- queries (rotated forward for MSE keys on compressed splits)
-  const bool rotate = kMse && !ring_split;
-  for (int e = tid; e < G * D; e += kDecThreads) {
+  for (int e = tid; e < G * D; e += kRingThreads) {
     const int g = e / D, j = e % D;
-    float qv = load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + j);
-    if (rotate && ((p.sign_words[j >> 5] >> (j & 31)) & 1u)) qv = -qv;
-    q_s[g][j] = qv;
+    q_s[g][j] = load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + j);
   }
   __syncthreads();
-  if (rotate) {
-    constexpr int B = D & (-D);
-    for (int hh = 1; hh < B; hh <<= 1) {
-      for (int e = tid; e < G * (D / 2); e += kDecThreads) {
-        const int g = e / (D / 2), pr = e % (D / 2);
-        const int j = (pr / hh) * (2 * hh) + (pr % hh);
-        const float a = q_s[g][j], c = q_s[g][j + hh];
-        q_s[g][j] = a + c;
-        q_s[g][j + hh] = a - c;
-      }
-      __syncthreads();
-    }
-    const float rb = rsqrtf(static_cast<float>(B));
-    for (int e = tid; e < G * D; e += kDecThreads) q_s[e / D][e % D] *= rb;
-    __syncthreads();
-  }
 
-  // running max / sum of query head tid (threads tid < G)
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;  // of query head tid (tid < G)
   float acc[kAccPerThread];
 #pragma unroll
   for (int a = 0; a < kAccPerThread; ++a) acc[a] = 0.0f;
   const int jj = tid % D;
   const int grp = tid / D;
 
-  for (int tile = begin; tile < end; tile += kTile) {
+  for (int tile = 0; tile < end; tile += kTile) {
     const int ntok = min(kTile, end - tile);
-    bool tile_ok = true;
-    if (!ring_split) {
-      // stage the tile's 16 contiguous slots
-      const int lblk = tile / p.block_size;
-      const int off = tile % p.block_size;
-      const int phys = p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + lblk];
-      tile_ok = phys >= 0 && phys < p.num_blocks;
-      if (tile_ok) {
-        const uint8_t *src = p.pool + ((static_cast<int64_t>(phys) * p.num_kv_heads + h) * p.block_size + off) *
-                                          static_cast<int64_t>(p.slot_bytes);
-        const int nvec = (kTile * p.slot_bytes) / 16;
-        for (int e = tid; e < nvec; e += kDecThreads)
-          reinterpret_cast<uint4 *>(run_s)[e] = reinterpret_cast<const uint4 *>(src)[e];
-      }
-    }
-    __syncthreads();
-    // decode the tile to fp32 (keys in the rotated basis for MSE)
-    for (int e = tid; e < kTile * D; e += kDecThreads) {
+    for (int e = tid; e < kTile * D; e += kRingThreads) {
       const int t = e / D, j = e % D;
       float kv = 0.0f, vv = 0.0f;
       if (t < ntok) {
-        if (ring_split) {
-          const int64_t ro = ((static_cast<int64_t>(b) * p.num_kv_heads + h) * p.ring_cap + tile + t) * D + j;
-          kv = bf16_bits_to_float(p.ring_k[ro]);
-          vv = bf16_bits_to_float(p.ring_v[ro]);
-        } else if (tile_ok) {
-          const uint8_t *slot = run_s + t * p.slot_bytes;
-          if constexpr (kMse) {
-            const int bit = j * KB;
-            const uint32_t w = static_cast<uint32_t>(slot[bit >> 3]) | (static_cast<uint32_t>(slot[(bit >> 3) + 1]) << 8);
-            kv = cent_s[(w >> (bit & 7)) & ((1u << KB) - 1u)];
-          } else {
-            kv = e4m3fn_to_float(slot[j]);
-          }
-          const uint8_t *vf = slot + p.key_bytes;
-          const int vbit = j * VB;
-          const uint32_t w = static_cast<uint32_t>(vf[vbit >> 3]) | (static_cast<uint32_t>(vf[(vbit >> 3) + 1]) << 8);
-          const uint32_t code = (w >> (vbit & 7)) & ((1u << VB) - 1u);
-          const uint32_t sb = vf[kValCodeBytes] | (static_cast<uint32_t>(vf[kValCodeBytes + 1]) << 8);
-          const uint32_t zb = vf[kValCodeBytes + 2] | (static_cast<uint32_t>(vf[kValCodeBytes + 3]) << 8);
-          vv = fmaf(f16_bits_to_float(sb), static_cast<float>(code), f16_bits_to_float(zb));
-        }
+        const int64_t ro = ((static_cast<int64_t>(b) * p.num_kv_heads + h) * p.ring_cap + tile + t) * D + j;
+        kv = bf16_bits_to_float(p.ring_k[ro]);
+        vv = bf16_bits_to_float(p.ring_v[ro]);
       }
       k_s[t][j] = kv;
       v_s[t][j] = vv;
     }
     __syncthreads();
-    // per-token score factor
-    if (tid < kTile) {
-      float f = 1.0f;
-      if (kMse && !ring_split && tid < ntok && tile_ok) {
-        const uint8_t *slot = run_s + tid * p.slot_bytes;
-        f = f16_bits_to_float(slot[kKeyIdxBytes] | (static_cast<uint32_t>(slot[kKeyIdxBytes + 1]) << 8));
-        if (p.norm_correction) {
-          float ss = 0.0f;
-          for (int j = 0; j < D; ++j) ss = fmaf(k_s[tid][j], k_s[tid][j], ss);
-          f = f / sqrtf(ss);
-        }
-      }
-      f_s[tid] = f;
-    }
-    __syncthreads();
-    // scores (log2 domain)
-    for (int e = tid; e < G * kTile; e += kDecThreads) {
+    for (int e = tid; e < G * kTile; e += kRingThreads) {
       const int g = e / kTile, t = e % kTile;
       float s = -INFINITY;
-      if (t < ntok && (ring_split || tile_ok)) {
+      if (t < ntok) {
         float d = 0.0f;
         for (int j = 0; j < D; ++j) d = fmaf(q_s[g][j], k_s[t][j], d);
-        s = d * f_s[t] * p.scale_log2;
+        s = d * p.scale_log2;
       }
       p_s[g][t] = s;
     }
     __syncthreads();
-    // online softmax bookkeeping, one thread per query head
     if (tid < G) {
       const int g = tid;
       float mt = -INFINITY;
@@ -190,7 +592,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
       alpha_s[g] = alpha;
     }
     __syncthreads();
-    // value accumulation
     if (grp < kGroups) {
 #pragma unroll
       for (int a = 0; a < kAccPerThread; ++a) {
@@ -205,20 +606,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     __syncthreads();
   }
 
-  // ---- partials
-  const int64_t stride = D + 2;
+  const int pstride = partial_stride(D);
   if (grp < kGroups) {
 #pragma unroll
     for (int a = 0; a < kAccPerThread; ++a) {
       const int g = grp + a * kGroups;
       if (g < G) {
-        float *dst = p.partials + ((static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * p.splits_total + split) * stride;
-        dst[2 + jj] = acc[a];
+        float *dst = p.partials + ((static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * p.splits_total + split) * pstride;
+        dst[4 + jj] = acc[a];
       }
     }
   }
   if (tid < G) {
-    float *dst = p.partials + ((static_cast<int64_t>(b) * p.num_q_heads + h * G + tid) * p.splits_total + split) * stride;
+    float *dst = p.partials + ((static_cast<int64_t>(b) * p.num_q_heads + h * G + tid) * p.splits_total + split) * pstride;
     dst[0] = m_run;
     dst[1] = l_run;
   }
@@ -229,17 +629,18 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int j = threadIdx.x;
-  const float *part = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + hq) * p.splits_total * (D + 2);
+  const int ps = partial_stride(D);
+  const float *part = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + hq) * p.splits_total * ps;
   float m = -INFINITY;
-  for (int s = 0; s < p.splits_total; ++s) m = fmaxf(m, part[s * (D + 2)]);
+  for (int s = 0; s < p.splits_total; ++s) m = fmaxf(m, part[s * ps]);
   float l = 0.0f, o = 0.0f;
   if (m != -INFINITY) {
     for (int s = 0; s < p.splits_total; ++s) {
-      const float ms = part[s * (D + 2)];
+      const float ms = part[s * ps];
       if (ms == -INFINITY) continue;
       const float w = exp2f(ms - m);
-      l = fmaf(part[s * (D + 2) + 1], w, l);
-      o = fmaf(part[s * (D + 2) + 2 + j], w, o);
+      l = fmaf(part[s * ps + 1], w, l);
+      o = fmaf(part[s * ps + 4 + j], w, o);
     }
   }
   p.out[(static_cast<int64_t>(b) * p.num_q_heads + hq) * D + j] = (l > 0.0f) ? o / l : 0.0f;
@@ -248,10 +649,18 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
 template <int D, int KB, int VB>
 int launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
-  const dim3 grid(p.splits_total, p.num_kv_heads, p.batch);
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB>), grid, dim3(kDecThreads), 0, s, p, static_cast<int>(q_dtype));
-  int err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  const int qd = static_cast<int>(q_dtype);
+  if (p.num_splits > 0) {
+    const dim3 grid((p.num_splits + kWaves - 1) / kWaves, p.num_kv_heads, p.batch);
+    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB>), grid, dim3(64 * kWaves), 0, s, p, qd);
+    const int err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (p.splits_total > p.num_splits) {
+    hipLaunchKernelGGL((decode_ring_kernel<D>), dim3(1, p.num_kv_heads, p.batch), dim3(kRingThreads), 0, s, p, qd);
+    const int err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(p.num_q_heads, p.batch), dim3(D), 0, s, p);
   return hipGetLastError();
 }

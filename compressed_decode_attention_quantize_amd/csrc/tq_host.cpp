@@ -75,6 +75,37 @@ uint64_t splitmix64_next(uint64_t &state) {
 
 bool supported_head_dim(int d) { return d == 64 || d == 96 || d == 128; }
 
+// IEEE binary16 value of a positive normal float (round to nearest even).
+double f16_round(float v) {
+  int e;
+  std::frexp(static_cast<double>(v), &e);  // v = m * 2^e, m in [0.5, 1)
+  const double unit = std::ldexp(1.0, e - 11);  // f16 spacing in this binade
+  return std::nearbyint(static_cast<double>(v) / unit) * unit;
+}
+
+// sigma = 1 + i/2^18 minimising the largest relative error of
+// fp16(fp32(sigma * c_k)) over the table's positive levels.
+float best_centroid_scale(const float *c, int n) {
+  constexpr int kSteps = 1 << 18;
+  float best_s = 1.0f;
+  double best_e = INFINITY;
+  for (int i = 0; i < kSteps; ++i) {
+    const float sg = 1.0f + static_cast<float>(i) / static_cast<float>(kSteps);
+    double worst = 0.0;
+    for (int k = n / 2; k < n; ++k) {
+      const float prod = c[k] * sg;
+      const double e = std::fabs(f16_round(prod) - static_cast<double>(prod)) / static_cast<double>(prod);
+      if (e > worst) worst = e;
+      if (worst >= best_e) break;
+    }
+    if (worst < best_e) {
+      best_e = worst;
+      best_s = sg;
+    }
+  }
+  return best_s;
+}
+
 }  // namespace
 
 tq_status fail(tq_status st, const std::string &msg) {
@@ -85,14 +116,20 @@ tq_status fail(tq_status st, const std::string &msg) {
 void clear_error() { g_last_error.clear(); }
 
 tq_status check_config(const tq_config *cfg) {
+  // Cheap per-call validation: the fields and the derived sizes (the tables
+  // are trusted to be the ones tq_config_init wrote).
   if (!cfg) return fail(TQ_ERR_INVALID_ARG, "config is NULL");
-  tq_config ref;
-  if (tq_config_init(cfg->head_dim, cfg->key_quant_bits, cfg->value_quant_bits,
-                     cfg->norm_correction, cfg->seed, &ref) != TQ_OK)
-    return TQ_ERR_INVALID_ARG;
-  if (ref.slot_size_aligned != cfg->slot_size_aligned || ref.key_packed_size != cfg->key_packed_size ||
-      ref.value_packed_size != cfg->value_packed_size || ref.wht_block != cfg->wht_block ||
-      ref.key_fp8 != cfg->key_fp8 || ref.n_centroids != cfg->n_centroids)
+  const int d = cfg->head_dim, kb = cfg->key_quant_bits, vb = cfg->value_quant_bits;
+  if (!supported_head_dim(d) || (kb != 3 && kb != 4 && kb != 8) || (vb != 3 && vb != 4))
+    return fail(TQ_ERR_INVALID_ARG, "config has an unsupported head_dim / bit width");
+  const int fp8 = kb == 8;
+  const int kp = fp8 ? d : ceil_div_i(d * kb, 8) + 2;
+  const int vp = ceil_div_i(d * vb, 8) + 4;
+  const int mse = fp8 ? vb : kb;
+  if (cfg->key_fp8 != fp8 || cfg->key_packed_size != kp || cfg->value_packed_size != vp ||
+      cfg->slot_size != kp + vp || cfg->slot_size_aligned != kp + vp + ((kp + vp) % 2) ||
+      cfg->wht_block != (d & (-d)) || cfg->n_centroids != (1 << mse) ||
+      !(cfg->centroid_scale >= 1.0f && cfg->centroid_scale < 2.0f))
     return fail(TQ_ERR_INVALID_ARG, "config was modified after tq_config_init");
   clear_error();
   return TQ_OK;
@@ -129,7 +166,7 @@ tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_
   plan->splits_total = plan->num_splits + (ring_cap > 0 ? 1 : 0);
   if (plan->splits_total == 0) plan->splits_total = 1;  // empty context still writes zeros
   plan->workspace_bytes = static_cast<size_t>(batch) * num_q_heads * plan->splits_total *
-                          (cfg.head_dim + 2) * sizeof(float);
+                          (cfg.head_dim + 4) * sizeof(float);  // [m, l, -, -, acc[D]]
   return TQ_OK;
 }
 
@@ -174,6 +211,7 @@ TQ_EXPORT tq_status tq_config_init(int head_dim, int key_bits, int value_bits, i
     c.centroids[k] = static_cast<float>(c64[k]);
   }
   for (int k = 0; k + 1 < c.n_centroids; ++k) c.midpoints[k] = static_cast<float>((c64[k] + c64[k + 1]) / 2.0);
+  c.centroid_scale = best_centroid_scale(c.centroids, c.n_centroids);
   *out = c;
   clear_error();
   return TQ_OK;

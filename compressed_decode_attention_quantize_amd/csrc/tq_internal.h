@@ -67,7 +67,7 @@ struct DecodeParams {
   const uint16_t *ring_k;  // bf16 bits
   const uint16_t *ring_v;
   const int32_t *ring_lens;
-  float *partials;         // [batch][Hq][splits_total][D + 2]
+  float *partials;         // [batch][Hq][splits_total][D + 4]: m, l, pad, pad, acc[D]
   float *out;
   int64_t num_blocks;
   int32_t batch;
@@ -84,6 +84,7 @@ struct DecodeParams {
   int32_t key_bytes;
   int32_t norm_correction;
   float scale_log2;        // softmax scale * log2(e)
+  float centroid_scale;    // sigma of the f16 centroid table
   uint32_t sign_words[4];
   float centroids[16];
 };

@@ -73,6 +73,8 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
  *   float64 levels).
  * wht_block: length B of the blockwise Walsh-Hadamard transform, the largest
  *   power of two dividing head_dim (128 -> 128, 96 -> 32, 64 -> 64).
+ * centroid_scale: sigma = 1 + i / 2^18 (i < 2^18) minimising the largest
+ *   relative round-off of fp16(fp32(sigma * centroid)) over the table.
  */
 typedef struct {
   int32_t head_dim;          /* 64 | 96 | 128                                 */
@@ -92,6 +94,9 @@ typedef struct {
   int32_t wht_block;
   float centroids[16];
   float midpoints[15];
+  float centroid_scale;      /* sigma in [1, 2): the f16 images of sigma * centroids
+                                are closest to exact; used by the decode kernel's
+                                f16 centroid table (the score divides by sigma) */
 } tq_config;
 
 /* Dataclass constructor ([API] TurboQuantConfig fields). head_dim must be 64,

@@ -133,10 +133,10 @@ def test_decode_argument_errors_before_launch():
 def test_workspace_size_and_plan():
     c = tq.config_from_preset("turboquant_k8v4", 128)
     b, n = tq.decode_workspace_size(c, 16, 32, 8192, 0, 256)
-    assert n == 32 and b == 16 * 32 * 32 * 130 * 4
+    assert n == 32 and b == 16 * 32 * 32 * 132 * 4
     b, n = tq.decode_workspace_size(c, 16, 32, 8192, 128, 256)
     assert n == 33
     b, n = tq.decode_workspace_size(c, 4, 8, 0, 0, 0)
-    assert n == 1 and b == 4 * 8 * 1 * 130 * 4
+    assert n == 1 and b == 4 * 8 * 1 * 132 * 4
     _, n_auto = tq.decode_workspace_size(c, 16, 32, 8192)
     assert n_auto >= 1

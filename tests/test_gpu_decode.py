@@ -94,6 +94,7 @@ def test_decode_matches_oracle(name, split):
     cfg, ocfg, pool_np, tables, q, ring = _scenario(d, kb, vb, nc, hq, hkv, lens, rl, rc, seed=sum(name.encode()))
     got, want = _run(cfg, ocfg, pool_np, tables, lens, q, ring, split_tokens=split)
     err = per_head_rel_l2(got, want)
+    announce(f"  rel L2 {err:.2e}")
     assert err <= ATTN_RTOL, err
 
 
@@ -123,7 +124,9 @@ def test_gqa_group_sizes(g):
     hkv = 2
     cfg, ocfg, pool_np, tables, q, ring = _scenario(128, 3, 4, True, g * hkv, hkv, [300, 47], seed=g)
     got, want = _run(cfg, ocfg, pool_np, tables, [300, 47], q, ring)
-    assert per_head_rel_l2(got, want) <= ATTN_RTOL
+    err = per_head_rel_l2(got, want)
+    announce(f"  rel L2 {err:.2e}")
+    assert err <= ATTN_RTOL
 
 
 @pytest.mark.parametrize("qdt", ["f32", "f16"])
@@ -155,9 +158,18 @@ def test_split_invariance_and_determinism():
     announce("decode split invariance")
     lens = [1777, 900, 3]
     cfg, ocfg, pool_np, tables, q, ring = _scenario(128, 4, 4, True, 16, 4, lens, [40, 128, 0], 128, seed=4)
-    outs = [_run(cfg, ocfg, pool_np, tables, lens, q, ring, split_tokens=s)[0] for s in (16, 64, 256, 2048)]
+    runs = [_run(cfg, ocfg, pool_np, tables, lens, q, ring, split_tokens=s) for s in (16, 64, 256, 2048)]
+    outs = [r[0] for r in runs]
+    # every split choice meets the oracle bound; between themselves they
+    # differ only by fp32 summation order (weights are carried to ~22 bits)
+    for got, want in runs:
+        err = per_head_rel_l2(got, want)
+        announce(f"  rel L2 {err:.2e}")
+        assert err <= ATTN_RTOL
     for o in outs[1:]:
-        assert np.allclose(o, outs[0], rtol=1e-5, atol=1e-6)
+        d = per_head_rel_l2(o, outs[0])
+        announce(f"  split-to-split {d:.2e}")
+        assert d <= 1e-4
     again = _run(cfg, ocfg, pool_np, tables, lens, q, ring, split_tokens=64)[0]
     assert np.array_equal(again.view(np.uint32), outs[1].view(np.uint32))
 
