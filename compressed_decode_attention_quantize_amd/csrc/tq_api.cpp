@@ -106,6 +106,8 @@ TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, con
   if (st != TQ_OK) return st;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: need batch >= 0 and num_q_heads a positive multiple of num_kv_heads");
+  if (batch > 8192)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: at most 8192 sequences per call");
   if (num_q_heads / num_kv_heads > 16)
     return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: at most 16 query heads per KV head");
   if (block_size <= 0 || block_size % 16 != 0)
@@ -137,7 +139,6 @@ TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, con
   p.ring_k = static_cast<const uint16_t *>(ring_k);
   p.ring_v = static_cast<const uint16_t *>(ring_v);
   p.ring_lens = ring_lens;
-  p.partials = static_cast<float *>(workspace);
   p.out = out;
   p.num_blocks = num_blocks;
   p.batch = batch;
@@ -148,8 +149,10 @@ TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, con
   p.max_seq_len = max_seq_len;
   p.ring_cap = has_ring ? ring_cap : 0;
   p.split_tokens = plan.split_tokens;
-  p.num_splits = plan.num_splits;
+  p.max_splits = plan.max_splits;
   p.splits_total = plan.splits_total;
+  p.plan = static_cast<int32_t *>(workspace);
+  p.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.header_bytes);
   p.slot_bytes = cfg->slot_size_aligned;
   p.key_bytes = cfg->key_packed_size;
   p.norm_correction = cfg->norm_correction;

@@ -31,6 +31,11 @@
 //  16x16x16 f16: lane l holds A[l%16][4(l/16)+e], B[4(l/16)+e][l%16], e<4;
 //  both: result lane l register r = D[4(l/16)+r][l%16].
 
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -49,6 +54,21 @@ constexpr int kPartStride_pad = 4;      // partial = [m, l, -, -, acc[D]]
 
 __device__ __forceinline__ int partial_stride(int d) { return d + kPartStride_pad; }
 
+// Active waves of the decode: all W launched waves, but no wave with fewer
+// than min_tiles tiles (min_tokens / 16; 256 tokens when the caller passes 0).
+constexpr int kDefaultMinTokens = 256;
+__host__ __device__ __forceinline__ int work_waves(long long total_tiles, int launched, int min_tokens) {
+  const long long min_tiles = (min_tokens > 0 ? min_tokens : kDefaultMinTokens) / kTile;
+  long long w = total_tiles / min_tiles;
+  if (w < 1) w = 1;
+  return static_cast<int>(w < launched ? w : launched);
+}
+
+// The wave whose range [w T / W, (w+1) T / W) holds flattened tile f.
+__host__ __device__ __forceinline__ int first_wave(long long f, long long total, int active) {
+  return static_cast<int>(((f + 1) * active - 1) / total);
+}
+
 // Compile-time geometry of one (head_dim, key bits, value bits) variant.
 template <int D, int KB, int VB>
 struct Geo {
@@ -63,13 +83,44 @@ struct Geo {
   static constexpr int kTileBytes = kTile * kSlot;
   static constexpr int kTileChunks = kTileBytes / 16;           // 16-byte chunks
   static constexpr int kChunksPerLane = (kTileChunks + 63) / 64;
-  static constexpr int kQBytes = 2 * 16 * D * 2;    // f16 rotated queries, hi and lo [2][16][D]
-  // one wave's LDS: the staged tile or the rotated queries, plus slack for
-  // the funnel-shifted reads that run up to 7 bytes past a field
-  static constexpr int kScratch = (kTileBytes > kQBytes ? kTileBytes : kQBytes) + 16;
+  static constexpr int kQBytes = 16 * D * 2;        // one f16 plane of rotated queries [16][D]
+  // a tile buffer: the tile plus slack for the funnel-shifted reads that run
+  // up to 7 bytes past a field, rounded to 16 bytes
+  static constexpr int kTileBuf = ((kTileBytes + 16) + 15) / 16 * 16;
+  // one wave's LDS: two tile buffers (double buffering), or the queries
+  static constexpr int kScratch = (2 * kTileBuf > kQBytes ? 2 * kTileBuf : kQBytes);
   static constexpr int kLut = KB == 4 ? 256 : (KB == 3 ? 64 : 1);
   static_assert(kSlot % 2 == 0, "slot size must be even");
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Byte offset of an LDS object (the value an LDS-address-space pointer holds).
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)(p)));
+}
+
+// Direct HBM -> LDS load of 16 bytes per lane: lane l's bytes land at LDS
+// offset lds_base + 16 l (lds_base is wave-uniform). Issued as inline asm so
+// the compiler does not hold later LDS reads of other buffers behind it;
+// callers wait for it with wait_vmcnt before reading the destination.
+__device__ __forceinline__ void load_lds_16(const void *gaddr, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(gaddr)
+      : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (s_waitcnt vmcnt(N); the other counters are left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 template <int N>
 struct Words {
@@ -244,7 +295,7 @@ __device__ __forceinline__ uint32_t lds_u16(const uint32_t *words, uint32_t off)
 }
 
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeParams p, int q_dtype) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D == 96 ? 2 : 3))) void decode_split_kernel(DecodeParams p, int q_dtype) {
   using GE = Geo<D, KB, VB>;
   using VX = ValueExpand<VB>;
   constexpr int S = GE::kSlot;
@@ -265,42 +316,92 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeParams 
       lut[e] = f16_pair_bits(p.centroids[lo] * p.centroid_scale, p.centroids[hi] * p.centroid_scale);
     }
   }
-  __syncthreads();  // the only workgroup barrier; waves are independent below
-
-  // the wave index is uniform across the wave: say so, so that the split
-  // bookkeeping, block-table reads and tile addresses stay in scalar registers
-  const int split = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(wave);
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  if (split >= p.num_splits) return;
-  const int G = p.num_q_heads / p.num_kv_heads;
-  int len = p.seq_lens[b];
-  len = min(max(len, 0), min(p.max_seq_len, p.max_blocks_per_seq * p.block_size));
-  const int begin = split * p.split_tokens;
-  const int end = min(len, begin + p.split_tokens);
-  const int pstride = partial_stride(D);
-  float *part_base = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + h * G) * p.splits_total * pstride +
-                     static_cast<int64_t>(split) * pstride;
-
-  if (begin >= end) {
-    // empty split: identity partial
-    if (lane < G) {
-      float *dst = part_base + static_cast<int64_t>(lane) * p.splits_total * pstride;
-      dst[0] = -INFINITY;
-      dst[1] = 0.0f;
-    }
-    return;
+  // ---- work division, computed by every workgroup from the device-side
+  // lengths. The (sequence, KV head, 16-token tile) triples are flattened in
+  // that order; wave w of the W active waves takes the contiguous range
+  // [w T / W, (w+1) T / W) of the T tiles (at least min_tiles each), so every
+  // wave streams the same number of tiles whatever the length mix. A wave
+  // writes one partial per (sequence, KV head) segment it covers; the
+  // segment's slot is its wave index minus the first wave of the segment.
+  extern __shared__ int32_t seq_prefix[];  // [batch + 1]: tiles of sequences < b
+  __shared__ int32_t scan_s[64 * kWaves];
+  const int tid = threadIdx.x;
+  const int B = p.batch;
+  const int Hkv = p.num_kv_heads;
+  const int seq_cap = min(p.max_seq_len, p.max_blocks_per_seq * p.block_size);
+  const int per = (B + 64 * kWaves - 1) / (64 * kWaves);
+  const int b_lo = min(B, tid * per), b_hi = min(B, b_lo + per);
+  int local = 0;
+  for (int bb = b_lo; bb < b_hi; ++bb) local += (min(max(p.seq_lens[bb], 0), seq_cap) + kTile - 1) / kTile;
+  scan_s[tid] = local;
+  __syncthreads();  // also publishes the code-pair table
+  for (int off = 1; off < 64 * kWaves; off <<= 1) {
+    const int v = tid >= off ? scan_s[tid - off] : 0;
+    __syncthreads();
+    scan_s[tid] += v;
+    __syncthreads();
   }
+  {
+    int run = scan_s[tid] - local;
+    for (int bb = b_lo; bb < b_hi; ++bb) {
+      seq_prefix[bb] = run;
+      run += (min(max(p.seq_lens[bb], 0), seq_cap) + kTile - 1) / kTile;
+    }
+    if (tid == 64 * kWaves - 1) seq_prefix[B] = scan_s[tid];
+  }
+  __syncthreads();  // the last workgroup barrier; waves are independent below
+  const long long total = static_cast<long long>(seq_prefix[B]) * Hkv;  // T
+  const int active = work_waves(total, gridDim.x * kWaves, p.split_tokens);
+  if (blockIdx.x == 0) {
+    // header for the reduce kernel: T, W and the per-sequence tile prefix
+    for (int bb = tid; bb <= B; bb += 64 * kWaves) p.plan[4 + bb] = seq_prefix[bb];
+    if (tid == 0) {
+      reinterpret_cast<long long *>(p.plan)[0] = total;
+      p.plan[2] = active;
+    }
+  }
+  const int G = p.num_q_heads / Hkv;
+  const int pstride = partial_stride(D);
+  // the wave index is uniform across the wave: say so, so that the range
+  // bookkeeping, block-table reads and tile addresses stay in scalar registers
+  const int w = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(wave);
+  if (w >= active) return;
+  long long f = static_cast<long long>(w) * total / active;
+  const long long f_end = static_cast<long long>(w + 1) * total / active;
+  while (f < f_end) {
+  int lo = 0, hi = B - 1;  // largest b with seq_prefix[b] * Hkv <= f
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (static_cast<long long>(__builtin_amdgcn_readfirstlane(seq_prefix[mid])) * Hkv <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo;
+  const int pb = __builtin_amdgcn_readfirstlane(seq_prefix[b]);
+  const int nb = __builtin_amdgcn_readfirstlane(seq_prefix[b + 1]) - pb;  // tiles of the sequence
+  const long long seg0 = static_cast<long long>(pb) * Hkv;
+  const int h = static_cast<int>((f - seg0) / nb);
+  const long long seg_start = seg0 + static_cast<long long>(h) * nb;   // first tile of (b, h)
+  const long long seg_stop = seg_start + nb;
+  const long long run_end = seg_stop < f_end ? seg_stop : f_end;
+  const int slot = w - first_wave(seg_start, total, active);
+  const int len = min(max(p.seq_lens[b], 0), seq_cap);
+  const int begin = static_cast<int>(f - seg_start) * kTile;
+  const int end = min(len, static_cast<int>(run_end - seg_start) * kTile);
+  f = run_end;
+  float *part_base = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + h * G) * p.splits_total * pstride +
+                     static_cast<int64_t>(slot) * pstride;
 
   uint32_t *scr = scratch[wave];  // this wave's LDS: queries, then the staged tile
 
-  // ---- rotated queries (f16) -> LDS [16][D], then into MFMA B operands
+  // ---- rotated queries as f16 hi + lo parts, in the MFMA B-operand layout
+  half8_t qf[KM], ql[KM];
   {
     using T = Team<D>;
     const int team = lane / T::kLanes;
     const int r = lane - team * T::kLanes;
-    const int rows_per_pass = T::kPerWave;
-    _Float16 *qs = reinterpret_cast<_Float16 *>(scr);
+    constexpr int rows_per_pass = T::kPerWave;
+    constexpr int kPasses = (16 + rows_per_pass - 1) / rows_per_pass;
+    u32x4_t qhi[kPasses], qlo[kPasses];
     for (int g0 = 0; g0 < 16; g0 += rows_per_pass) {
       const int g = g0 + team;
       float x[8];
@@ -319,29 +420,34 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeParams 
         for (int i = 0; i < 8; ++i) x[i] *= rb;
       }
       if (team < rows_per_pass && g < 16) {
-        u32x4_t v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = f16_pair_bits(x[2 * i], x[2 * i + 1]);
-        *reinterpret_cast<u32x4_t *>(qs + g * D + 8 * r) = v;
-        // the low parts go to the second half of the scratch
+        u32x4_t hv, lv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float h0 = f16_bits_to_float(v[i] & 0xffffu), h1 = f16_bits_to_float(v[i] >> 16);
-          v[i] = f16_pair_bits(x[2 * i] - h0, x[2 * i + 1] - h1);
+          hv[i] = f16_pair_bits(x[2 * i], x[2 * i + 1]);
+          const float h0 = f16_bits_to_float(hv[i] & 0xffffu), h1 = f16_bits_to_float(hv[i] >> 16);
+          lv[i] = f16_pair_bits(x[2 * i] - h0, x[2 * i + 1] - h1);
         }
-        *reinterpret_cast<u32x4_t *>(qs + 16 * D + g * D + 8 * r) = v;
+        qhi[g0 / rows_per_pass] = hv;
+        qlo[g0 / rows_per_pass] = lv;
       }
     }
-  }
-  half8_t qf[KM], ql[KM];  // rotated queries as f16 hi + lo parts
-  {
-    const _Float16 *qs = reinterpret_cast<const _Float16 *>(scr);
+    // hi parts through LDS into the MFMA operand layout, then the lo parts
+    _Float16 *qs = reinterpret_cast<_Float16 *>(scr);
 #pragma unroll
-    for (int m = 0; m < KM; ++m)
-      qf[m] = *reinterpret_cast<const half8_t *>(qs + col * D + kq * (D / 4) + 8 * m);
+    for (int phase = 0; phase < 2; ++phase) {
 #pragma unroll
-    for (int m = 0; m < KM; ++m)
-      ql[m] = *reinterpret_cast<const half8_t *>(qs + 16 * D + col * D + kq * (D / 4) + 8 * m);
+      for (int k = 0; k < kPasses; ++k) {
+        const int g = k * rows_per_pass + team;
+        if (team < rows_per_pass && g < 16)
+          *reinterpret_cast<u32x4_t *>(qs + g * D + 8 * r) = phase == 0 ? qhi[k] : qlo[k];
+      }
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        const half8_t v = *reinterpret_cast<const half8_t *>(qs + col * D + kq * (D / 4) + 8 * m);
+        if (phase == 0) qf[m] = v;
+        else ql[m] = v;
+      }
+    }
   }
 
   // ---- tile loop
@@ -350,44 +456,63 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeParams 
   for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_lane = 0.0f, z_lane = 0.0f;
 
-  u32x4_t pre[GE::kChunksPerLane];
-  bool pre_ok = false;
-  auto issue = [&](int tile0) {
+  // Tiles go HBM -> LDS by direct loads (global_load_lds_dwordx4: lane l of
+  // a load instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS window),
+  // double buffered: the next tile is in flight while this one is used.
+  constexpr int kLoads = GE::kChunksPerLane;     // load instructions per tile
+  // Block ids of the segment, 64 at a time: lane i holds the id of logical
+  // block blk_base + i; tiles pick theirs with readlane.
+  int blk_base = -1 << 30, blk_lane = 0;
+  bool ok_next = false;
+  auto issue = [&](int tile0, int bsel) {
     const int lblk = tile0 / p.block_size;
     const int off = tile0 - lblk * p.block_size;
-    const int phys = p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + lblk];
-    pre_ok = phys >= 0 && phys < p.num_blocks;
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
-        p.pool + ((static_cast<int64_t>(pre_ok ? phys : 0) * p.num_kv_heads + h) * p.block_size + off) *
-                     static_cast<int64_t>(S));
+    int phys;
+    if (lblk - blk_base >= 64) {
+      // refill the window; the wait for this load stays on this branch
+      blk_base = lblk;
+      const int bi = blk_base + lane;
+      const int last = (end - 1) / p.block_size;
+      blk_lane = bi <= last ? p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + bi] : 0;
+      phys = __builtin_amdgcn_readlane(blk_lane, 0);
+    } else {
+      phys = __builtin_amdgcn_readlane(blk_lane, lblk - blk_base);
+    }
+    ok_next = phys >= 0 && phys < p.num_blocks;
+    // an invalid block reads the pool's first tile instead (its tokens are masked)
+    const uint8_t *src = p.pool + ((static_cast<int64_t>(ok_next ? phys : 0) * p.num_kv_heads + h) * p.block_size + off) *
+                                      static_cast<int64_t>(S);
+    const uint32_t dst = lds_offset(scratch[wave]) + bsel * GE::kTileBuf;
 #pragma unroll
-    for (int k = 0; k < GE::kChunksPerLane; ++k) {
+    for (int k = 0; k < kLoads; ++k) {
       const int c = lane + 64 * k;
-      pre[k] = (pre_ok && c < GE::kTileChunks) ? src[c] : u32x4_t{0u, 0u, 0u, 0u};
+      if (c < GE::kTileChunks) load_lds_16(src + 16 * c, dst + 1024 * k);
     }
   };
-  issue(begin);
+  issue(begin, 0);
 
   const float c0 = static_cast<float>(VX::kC0);
   const float inv_sigma = 1.0f / p.centroid_scale;
-  for (int tile0 = begin; tile0 < end; tile0 += kTile) {
+  int bsel = 0;
+  for (int tile0 = begin; tile0 < end; tile0 += kTile, bsel ^= 1) {
     const int ntok = min(kTile, end - tile0);
-    const bool tile_ok = pre_ok;
-#pragma unroll
-    for (int k = 0; k < GE::kChunksPerLane; ++k) {
-      const int c = lane + 64 * k;
-      if (c < GE::kTileChunks) reinterpret_cast<u32x4_t *>(scr)[c] = pre[k];
+    const bool tile_ok = ok_next;
+    if (tile0 + kTile < end) {
+      issue(tile0 + kTile, bsel ^ 1);
+      wait_vmcnt<kLoads>();  // this tile's loads are done, the next tile's may run
+    } else {
+      wait_vmcnt<0>();
     }
-    if (tile0 + kTile < end) issue(tile0 + kTile);
+    const uint32_t *tw = scr + bsel * (GE::kTileBuf / 4);  // this tile's bytes as words
 
     // per-token scalars: lane t < 16 reads its slot's norm / scale / zero
     if (lane < 16) {
       const uint32_t slot = static_cast<uint32_t>(lane * S);
       const bool ok = tile_ok && lane < ntok;
       float fb = p.scale_log2;
-      if constexpr (GE::kMse) fb *= f16_bits_to_float(lds_u16(scr, slot + GE::kKeyCodeBytes));
-      const float s1 = f16_bits_to_float(lds_u16(scr, slot + GE::kKeyBytes + GE::kValCodeBytes));
-      const float z1 = f16_bits_to_float(lds_u16(scr, slot + GE::kKeyBytes + GE::kValCodeBytes + 2));
+      if constexpr (GE::kMse) fb *= f16_bits_to_float(lds_u16(tw, slot + GE::kKeyCodeBytes));
+      const float s1 = f16_bits_to_float(lds_u16(tw, slot + GE::kKeyBytes + GE::kValCodeBytes));
+      const float z1 = f16_bits_to_float(lds_u16(tw, slot + GE::kKeyBytes + GE::kValCodeBytes + 2));
       tok[wave][0][lane] = ok ? fb : -1.0f;  // negative marks a masked token
       tok[wave][1][lane] = ok ? s1 : 0.0f;
       tok[wave][2][lane] = ok ? fmaf(c0, s1, z1) : 0.0f;
@@ -395,7 +520,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeParams 
 
     // keys -> scores S^T[4kq + r][col]
     half8_t kf[KM];
-    key_operand<D, KB>(scr, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
+    key_operand<D, KB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
     float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int m = 0; m < KM; ++m) {
@@ -417,7 +542,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeParams 
       if (col < GE::kGroups) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const auto w = lds_bytes<VB>(scr, static_cast<uint32_t>((4 * kq + r) * S + GE::kKeyBytes + VB * col));
+          const auto w = lds_bytes<VB>(tw, static_cast<uint32_t>((4 * kq + r) * S + GE::kKeyBytes + VB * col));
           d[r] = w.w[0];
         }
       } else {
@@ -513,10 +638,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeParams 
       }
     }
   }
+  }  // segment loop
 }
 
-// Exact bf16 ring tokens (and the empty-context partial): fp32 VALU, one
-// workgroup per (sequence, KV head), partial index p.num_splits.
+// Exact bf16 ring tokens: fp32 VALU, one workgroup per (sequence, KV head),
+// partial slot p.max_splits of the sequence's query heads.
 constexpr int kRingThreads = 256;
 constexpr int kMaxG = 16;
 
@@ -534,8 +660,8 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int G = p.num_q_heads / p.num_kv_heads;
-  const int split = p.num_splits;
-  const int end = (p.ring_k != nullptr) ? min(max(p.ring_lens[b], 0), p.ring_cap) : 0;
+  const int split = p.max_splits;
+  const int end = min(max(p.ring_lens[b], 0), p.ring_cap);
 
   for (int e = tid; e < G * D; e += kRingThreads) {
     const int g = e / D, j = e % D;
@@ -631,32 +757,77 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
   const int j = threadIdx.x;
   const int ps = partial_stride(D);
   const float *part = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + hq) * p.splits_total * ps;
+  int nslots = 0;
+  if (p.max_splits > 0) {
+    // the split kernel's work division (header written before this launch)
+    const long long total = reinterpret_cast<const long long *>(p.plan)[0];
+    const int active = p.plan[2];
+    const int pb = p.plan[4 + b];
+    const int nb = p.plan[4 + b + 1] - pb;
+    if (nb > 0) {
+      const int h = hq / (p.num_q_heads / p.num_kv_heads);
+      const long long s0 = static_cast<long long>(pb) * p.num_kv_heads + static_cast<long long>(h) * nb;
+      nslots = first_wave(s0 + nb - 1, total, active) - first_wave(s0, total, active) + 1;
+    }
+  }
+  const bool ring = p.ring_cap > 0;
   float m = -INFINITY;
-  for (int s = 0; s < p.splits_total; ++s) m = fmaxf(m, part[s * ps]);
+  for (int s = 0; s < nslots; ++s) m = fmaxf(m, part[s * ps]);
+  if (ring) m = fmaxf(m, part[p.max_splits * ps]);
   float l = 0.0f, o = 0.0f;
   if (m != -INFINITY) {
-    for (int s = 0; s < p.splits_total; ++s) {
-      const float ms = part[s * ps];
+    for (int s = 0; s < nslots + (ring ? 1 : 0); ++s) {
+      const int slot = s < nslots ? s : p.max_splits;
+      const float ms = part[slot * ps];
       if (ms == -INFINITY) continue;
       const float w = exp2f(ms - m);
-      l = fmaf(part[s * ps + 1], w, l);
-      o = fmaf(part[s * ps + 4 + j], w, o);
+      l = fmaf(part[slot * ps + 1], w, l);
+      o = fmaf(part[slot * ps + 4 + j], w, o);
     }
   }
   p.out[(static_cast<int64_t>(b) * p.num_q_heads + hq) * D + j] = (l > 0.0f) ? o / l : 0.0f;
+}
+
+// Workgroups of the split kernel that fit on the device at once
+// (occupancy x compute units), cached per (kernel, device, LDS size).
+int resident_workgroups(const void *kernel, size_t dyn_lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void *, int, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const auto key = std::make_tuple(kernel, dev, dyn_lds);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kWaves, dyn_lds) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  const int n = std::max(1, per_cu) * std::max(1, cus);
+  std::lock_guard<std::mutex> g(mu);
+  cache[key] = n;
+  return n;
 }
 
 template <int D, int KB, int VB>
 int launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   const int qd = static_cast<int>(q_dtype);
-  if (p.num_splits > 0) {
-    const dim3 grid((p.num_splits + kWaves - 1) / kWaves, p.num_kv_heads, p.batch);
-    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB>), grid, dim3(64 * kWaves), 0, s, p, qd);
+  if (p.max_splits > 0) {
+    const size_t dyn = static_cast<size_t>(p.batch + 1) * sizeof(int32_t);
+    const void *kern = reinterpret_cast<const void *>(&decode_split_kernel<D, KB, VB>);
+    const int resident = resident_workgroups(kern, dyn);
+    if (resident < 0) return hipErrorInvalidValue;
+    // enough waves for the largest possible context, capped at what fits
+    const long long worst_tiles = static_cast<long long>(p.batch) * p.num_kv_heads * ((p.max_seq_len + kTile - 1) / kTile);
+    const long long need = (work_waves(worst_tiles, 1 << 30, p.split_tokens) + kWaves - 1) / kWaves;
+    const int grid = static_cast<int>(std::max(1LL, std::min<long long>(need, resident)));
+    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB>), dim3(grid), dim3(64 * kWaves), dyn, s, p, qd);
     const int err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (p.splits_total > p.num_splits) {
+  if (p.ring_cap > 0) {
     hipLaunchKernelGGL((decode_ring_kernel<D>), dim3(1, p.num_kv_heads, p.batch), dim3(kRingThreads), 0, s, p, qd);
     const int err = hipGetLastError();
     if (err != hipSuccess) return err;

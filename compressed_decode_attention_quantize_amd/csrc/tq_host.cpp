@@ -7,6 +7,7 @@
 // prhub summary of vLLM PR #39931 (TurboQuant page = block_size *
 // num_kv_heads * slot bytes).
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -148,25 +149,19 @@ tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_
                       int ring_cap, int split_tokens, SplitPlan *plan) {
   if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || ring_cap < 0)
     return fail(TQ_ERR_INVALID_ARG, "decode plan: negative batch/max_seq_len/ring_cap or num_q_heads <= 0");
-  int st = split_tokens;
-  if (st < 0 || st % 16 != 0)
+  if (split_tokens < 0 || split_tokens % 16 != 0)
     return fail(TQ_ERR_INVALID_ARG, "split_tokens must be 0 (auto) or a positive multiple of 16");
-  if (st == 0) {
-    // Aim for about 4096 (sequence, KV head, split) work items assuming 8 KV
-    // heads, with 256..2048 tokens per split.
-    const long long want_splits = std::max(1LL, (4096LL + 8LL * std::max(batch, 1) - 1) / (8LL * std::max(batch, 1)));
-    long long per = (max_seq_len + want_splits - 1) / want_splits;
-    per = ((per + 63) / 64) * 64;
-    if (per < 256) per = 256;
-    if (per > 2048) per = 2048;
-    st = static_cast<int>(per);
-  }
-  plan->split_tokens = st;
-  plan->num_splits = max_seq_len > 0 ? ceil_div_i(max_seq_len, st) : 0;
-  plan->splits_total = plan->num_splits + (ring_cap > 0 ? 1 : 0);
-  if (plan->splits_total == 0) plan->splits_total = 1;  // empty context still writes zeros
-  plan->workspace_bytes = static_cast<size_t>(batch) * num_q_heads * plan->splits_total *
-                          (cfg.head_dim + 4) * sizeof(float);  // [m, l, -, -, acc[D]]
+  // A wave covers at least min_tokens tokens (except the last wave of a
+  // short batch), so a (sequence, KV head) spans at most
+  // ceil(len / min_tokens) + 1 waves: one partial slot each.
+  const int min_tokens = split_tokens > 0 ? split_tokens : kMinTokensPerWave;
+  plan->split_tokens = split_tokens;
+  plan->max_splits = max_seq_len > 0 ? ceil_div_i(max_seq_len, min_tokens) + 1 : 0;
+  plan->splits_total = plan->max_splits + (ring_cap > 0 ? 1 : 0);
+  plan->header_bytes = ((16 + 4 * (static_cast<size_t>(batch) + 1) + 255) / 256) * 256;
+  plan->workspace_bytes = plan->header_bytes + static_cast<size_t>(batch) * num_q_heads *
+                                                   std::max(plan->splits_total, 1) * (cfg.head_dim + 4) *
+                                                   sizeof(float);  // rows [m, l, -, -, acc[D]]
   return TQ_OK;
 }
 

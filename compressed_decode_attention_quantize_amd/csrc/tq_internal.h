@@ -77,9 +77,10 @@ struct DecodeParams {
   int32_t max_blocks_per_seq;
   int32_t max_seq_len;
   int32_t ring_cap;
-  int32_t split_tokens;    // compressed tokens per split, multiple of 16
-  int32_t num_splits;      // compressed splits per sequence
-  int32_t splits_total;    // num_splits + (ring ? 1 : 0)
+  int32_t split_tokens;    // minimum tokens per wave (multiple of 16), or 0: 256
+  int32_t max_splits;      // partial slots per (sequence, q head) for compressed tokens
+  int32_t splits_total;    // max_splits + (ring ? 1 : 0): slot max_splits is the ring's
+  int32_t *plan;           // workspace header: [total tiles (int64), active waves, -, tile prefix[batch + 1]]
   int32_t slot_bytes;
   int32_t key_bytes;
   int32_t norm_correction;
@@ -97,11 +98,13 @@ int launch_decode(const tq_config &cfg, tq_dtype q_dtype, const DecodeParams &p,
 
 // Split plan shared by tq_decode_workspace_size and tq_decode_attention.
 struct SplitPlan {
-  int32_t split_tokens;
-  int32_t num_splits;
-  int32_t splits_total;
-  size_t workspace_bytes;
+  int32_t split_tokens;   // as given (0 = 256 tokens per wave at least)
+  int32_t max_splits;     // partial slots per (sequence, q head): ceil(max_seq_len / min tokens) + 1
+  int32_t splits_total;   // max_splits + ring slot
+  size_t header_bytes;    // work-division header (16 + 4 (batch + 1), rounded to 256)
+  size_t workspace_bytes; // header + partials
 };
+constexpr int kMinTokensPerWave = 256;
 tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_seq_len,
                       int ring_cap, int split_tokens, SplitPlan *plan);
 

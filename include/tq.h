@@ -157,11 +157,14 @@ tq_status tq_quantize_append(const tq_config *cfg, int layer_idx,
 
 /*
  * Workspace bytes for tq_decode_attention with the same arguments. The
- * decode splits each sequence's compressed context into chunks of
- * split_tokens tokens (0 = library choice; otherwise a positive multiple of
- * 16), plus one chunk for the ring when ring_cap > 0; the workspace holds one
- * (max, sum, acc[head_dim]) fp32 partial per (sequence, query head, chunk).
- * num_splits_out (nullable) receives the number of chunks per sequence.
+ * decode flattens the batch's (sequence, KV head, 16-token tile) triples and
+ * gives every resident wave an equal contiguous range of them, of at least
+ * split_tokens tokens (a positive multiple of 16; 0 means 256), so the work
+ * is balanced whatever the mix of lengths. The workspace holds a header
+ * (16 + 4 (batch + 1) bytes, rounded up to 256) and one fp32 partial
+ * (max, sum, acc[head_dim]) per (sequence, query head, slot) with
+ * ceil(max_seq_len / min tokens) + 1 slots, plus one for the ring when
+ * ring_cap > 0. num_splits_out (nullable) receives the slots per sequence.
  */
 tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, int num_q_heads,
                                    int max_seq_len, int ring_cap, int split_tokens,

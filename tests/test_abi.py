@@ -128,15 +128,20 @@ def test_decode_argument_errors_before_launch():
     assert _decode(c, split=24) == 1                   # split not a multiple of 16
     assert _decode(c, q=None) == 1
     assert _decode(c, batch=0) == 0                    # nothing to do
+    assert _decode(c, batch=9000) == 3                 # batch above the work-list limit
 
 
 def test_workspace_size_and_plan():
     c = tq.config_from_preset("turboquant_k8v4", 128)
+    # a wave covers >= 256 tokens, so a sequence spans <= 8192/256 + 1 waves
     b, n = tq.decode_workspace_size(c, 16, 32, 8192, 0, 256)
-    assert n == 32 and b == 16 * 32 * 32 * 132 * 4
+    assert n == 33 and b == 256 + 16 * 32 * 33 * 132 * 4
     b, n = tq.decode_workspace_size(c, 16, 32, 8192, 128, 256)
-    assert n == 33
+    assert n == 34
     b, n = tq.decode_workspace_size(c, 4, 8, 0, 0, 0)
-    assert n == 1 and b == 4 * 8 * 1 * 132 * 4
+    assert n == 0 and b == 256 + 4 * 8 * 1 * 132 * 4
     _, n_auto = tq.decode_workspace_size(c, 16, 32, 8192)
-    assert n_auto >= 1
+    assert n_auto == 33
+    # the header grows with the batch (tile prefix per sequence)
+    b, _ = tq.decode_workspace_size(c, 100, 8, 100, 0, 0)
+    assert b == 512 + 100 * 8 * 2 * 132 * 4
