@@ -129,6 +129,91 @@ def bulk_quantize(built, tq, torch, chunk=65536, reps=5):
     return n, ms
 
 
+def copy_probe(torch, nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of ``nbytes`` (torch copy_ of a float32
+    buffer): the measured copy bandwidth (read + write bytes / time), and the
+    reference kernel the PMC byte counters are scaled against."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms, "GBps": 2 * nbytes / (ms / 1e3) / 1e9}
+
+
+def _timed(torch, fn, reps):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def ring_flush(built, tq, torch, reps=10):
+    """One ring flush: every sequence's 128 ring tokens quantize-appended as a
+    chunk (one call, batch x ring tokens) into spare blocks of pool 0."""
+    from workloads import KVSource
+    from workloads import gpu as WG
+    w = built.w
+    n = w.batch * w.ring
+    k, v = KVSource(w, "cuda", stream_id=78).kv(n)
+    ids = torch.from_numpy(WG.spare_slot_ids(built, n)).cuda()
+    call = tq.prepare_quantize(built.cfg, 0, k, v, ids, built.pools[0])
+    call()
+    ms = _timed(torch, call, reps)
+    qbpt = WG.quantize_bytes_per_token(built)
+    return {"tokens": n, "ms": ms, "tokens_per_s": n / (ms / 1e3), "GBps": n * qbpt / (ms / 1e3) / 1e9}
+
+
+def concurrent_prefill(built, tq, torch, steps, reps=10):
+    """Decode on the current stream with a prefill quantize-append of
+    ``prefill_tokens`` tokens (a sequence outside the batch, written to spare
+    blocks) on a second stream: each alone, then both together."""
+    from workloads import gpu as WG
+    w = built.w
+    n = w.prefill_tokens
+    k, v = WG.prefill_source(w, "cuda").kv(n)
+    ids = torch.from_numpy(WG.spare_slot_ids(built, n)).cuda()
+    side = torch.cuda.Stream()
+    pre = tq.prepare_quantize(built.cfg, 0, k, v, ids, built.pools[0], stream=side.cuda_stream)
+    main = torch.cuda.current_stream()
+    dec = steps[0][1]
+
+    def prefill_alone():
+        side.wait_stream(main)
+        pre()
+        main.wait_stream(side)
+
+    def both():
+        side.wait_stream(main)
+        pre()
+        dec()
+        main.wait_stream(side)
+
+    prefill_alone()
+    both()
+    pre_ms = _timed(torch, prefill_alone, reps)
+    dec_ms = _timed(torch, dec, reps)
+    both_ms = _timed(torch, both, reps)
+    pbytes = n * WG.quantize_bytes_per_token(built)
+    dbytes = WG.decode_bytes(built)
+    return {"prefill_tokens": n, "prefill_ms": pre_ms, "prefill_tokens_per_s": n / (pre_ms / 1e3),
+            "prefill_GBps": pbytes / (pre_ms / 1e3) / 1e9, "decode_ms": dec_ms, "overlapped_ms": both_ms,
+            "overlapped_GBps": (pbytes + dbytes) / (both_ms / 1e3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,7 +247,8 @@ def main():
     n_pools = min(n_pools, 8)
     print(f"[bench] building {w.name}: {w.description}; {n_pools} pool(s) of {pool_bytes / 1e6:.1f} MB",
           file=sys.stderr, flush=True)
-    built = WG.build(w, "cuda", n_pools=n_pools, capture=(0,))
+    spare = (w.batch * -(-w.ring // w.block_size)) + -(-w.prefill_tokens // w.block_size)
+    built = WG.build(w, "cuda", n_pools=n_pools, capture=(0,), extra_blocks=spare)
     steps = WG.prepare_steps(built, args.split_tokens)
     _, nsplit = tq.decode_workspace_size(cfg, w.batch, w.num_q_heads, built.max_seq_len, w.ring, args.split_tokens)
 
@@ -201,6 +287,12 @@ def main():
 
     nq, qms = bulk_quantize(built, tq, torch)
     qbpt = WG.quantize_bytes_per_token(built)
+    extra = {}
+    if w.ring:
+        extra["ring_flush"] = ring_flush(built, tq, torch)
+    if w.prefill_tokens:
+        extra["concurrent_prefill"] = concurrent_prefill(built, tq, torch, steps)
+    extra["copy_probe"] = copy = copy_probe(torch)
 
     result = {
         "metric": "decode-attn KV tokens/s + achieved HBM GB/s (% peak); quantize tokens/s",
@@ -229,7 +321,9 @@ def main():
                           "GBps": nq * qbpt / (qms / 1e3) / 1e9, "bytes_per_token": qbpt},
         "roofline": {"bound": "hbm", "kernel": "tq_decode_attention (split + reduce kernels)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac_of_copy": achieved / copy["GBps"]},
+        **extra,
         "wall_s_timed": wall,
         "library": tq.version(),
     }

@@ -641,122 +641,181 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D =
   }  // segment loop
 }
 
-// Exact bf16 ring tokens: fp32 VALU, one workgroup per (sequence, KV head),
-// partial slot p.max_splits of the sequence's query heads.
+// Exact bf16 ring tokens: fp32 VALU, one workgroup per (sequence, KV head,
+// 64-token chunk of the ring), writing partial slot max_splits + chunk of the
+// sequence's query heads. K rows and V transposed go through LDS; scores
+// (thread = token x head group), softmax of the chunk (wave = head, lane =
+// token), then P.V (thread = output column x head group).
 constexpr int kRingThreads = 256;
 constexpr int kMaxG = 16;
 
-template <int D>
-__global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams p, int q_dtype) {
-  constexpr int kGroups = kRingThreads / D;
-  constexpr int kAccPerThread = (kMaxG + kGroups - 1) / kGroups;
-  __shared__ float q_s[kMaxG][D];
-  __shared__ float k_s[kTile][D + 1];
-  __shared__ float v_s[kTile][D + 1];
-  __shared__ float p_s[kMaxG][kTile];
-  __shared__ float alpha_s[kMaxG];
-
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int G = p.num_q_heads / p.num_kv_heads;
-  const int split = p.max_splits;
-  const int end = min(max(p.ring_lens[b], 0), p.ring_cap);
-
-  for (int e = tid; e < G * D; e += kRingThreads) {
-    const int g = e / D, j = e % D;
-    q_s[g][j] = load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + j);
-  }
-  __syncthreads();
-
-  float m_run = -INFINITY, l_run = 0.0f;  // of query head tid (tid < G)
-  float acc[kAccPerThread];
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int a = 0; a < kAccPerThread; ++a) acc[a] = 0.0f;
-  const int jj = tid % D;
-  const int grp = tid / D;
-
-  for (int tile = 0; tile < end; tile += kTile) {
-    const int ntok = min(kTile, end - tile);
-    for (int e = tid; e < kTile * D; e += kRingThreads) {
-      const int t = e / D, j = e % D;
-      float kv = 0.0f, vv = 0.0f;
-      if (t < ntok) {
-        const int64_t ro = ((static_cast<int64_t>(b) * p.num_kv_heads + h) * p.ring_cap + tile + t) * D + j;
-        kv = bf16_bits_to_float(p.ring_k[ro]);
-        vv = bf16_bits_to_float(p.ring_v[ro]);
-      }
-      k_s[t][j] = kv;
-      v_s[t][j] = vv;
-    }
-    __syncthreads();
-    for (int e = tid; e < G * kTile; e += kRingThreads) {
-      const int g = e / kTile, t = e % kTile;
-      float s = -INFINITY;
-      if (t < ntok) {
-        float d = 0.0f;
-        for (int j = 0; j < D; ++j) d = fmaf(q_s[g][j], k_s[t][j], d);
-        s = d * p.scale_log2;
-      }
-      p_s[g][t] = s;
-    }
-    __syncthreads();
-    if (tid < G) {
-      const int g = tid;
-      float mt = -INFINITY;
-      for (int t = 0; t < kTile; ++t) mt = fmaxf(mt, p_s[g][t]);
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
-      float lsum = 0.0f;
-      for (int t = 0; t < kTile; ++t) {
-        const float pt = (p_s[g][t] == -INFINITY) ? 0.0f : exp2f(p_s[g][t] - m_new);
-        p_s[g][t] = pt;
-        lsum += pt;
-      }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      alpha_s[g] = alpha;
-    }
-    __syncthreads();
-    if (grp < kGroups) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-      for (int a = 0; a < kAccPerThread; ++a) {
-        const int g = grp + a * kGroups;
-        if (g < G) {
-          float s = acc[a] * alpha_s[g];
-          for (int t = 0; t < kTile; ++t) s = fmaf(p_s[g][t], v_s[t][jj], s);
-          acc[a] = s;
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  const int pstride = partial_stride(D);
-  if (grp < kGroups) {
-#pragma unroll
-    for (int a = 0; a < kAccPerThread; ++a) {
-      const int g = grp + a * kGroups;
-      if (g < G) {
-        float *dst = p.partials + ((static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * p.splits_total + split) * pstride;
-        dst[4 + jj] = acc[a];
-      }
-    }
-  }
-  if (tid < G) {
-    float *dst = p.partials + ((static_cast<int64_t>(b) * p.num_q_heads + h * G + tid) * p.splits_total + split) * pstride;
-    dst[0] = m_run;
-    dst[1] = l_run;
-  }
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
 template <int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams p, int q_dtype) {
+  constexpr int kRow = D + 8;                       // bf16 per K row in LDS (16 bytes of padding)
+  constexpr int kTRow = kRingChunk + 8;             // bf16 per transposed V row
+  constexpr int kVec = D / 8;                       // 16-byte vectors per K/V row
+  constexpr int kHeadGroups = kRingThreads / D;     // P.V: threads per output column
+  constexpr int kAcc = (kMaxG + kHeadGroups - 1) / kHeadGroups;
+  constexpr int kScoreGroups = kRingThreads / kRingChunk;
+  constexpr int kScoreHeads = kMaxG / kScoreGroups;
+  __shared__ float q_s[kMaxG][D];
+  __shared__ __align__(16) uint16_t k_s[kRingChunk][kRow];
+  __shared__ __align__(16) uint16_t vt_s[D][kTRow];
+  __shared__ __align__(16) float p_s[kMaxG][kRingChunk];
+
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int chunk = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int c0 = chunk * kRingChunk;
+  const int n = min(max(min(max(p.ring_lens[b], 0), p.ring_cap) - c0, 0), kRingChunk);
+  const int pstride = partial_stride(D);
+  const int64_t part0 = static_cast<int64_t>(b) * p.num_q_heads + h * G;
+  const int slot = p.max_splits + chunk;
+
+  for (int e = tid; e < G * D; e += kRingThreads) {
+    const int g = e / D, j = e - (e / D) * D;
+    q_s[g][j] = load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + j);
+  }
+  const int64_t ring0 = ((static_cast<int64_t>(b) * p.num_kv_heads + h) * p.ring_cap + c0) * D;
+  for (int e = tid; e < kRingChunk * kVec; e += kRingThreads) {
+    const int t = e % kRingChunk, c = e / kRingChunk;
+    u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (t < n) {
+      kv = *reinterpret_cast<const u32x4_t *>(p.ring_k + ring0 + t * D + 8 * c);
+      vv = *reinterpret_cast<const u32x4_t *>(p.ring_v + ring0 + t * D + 8 * c);
+    }
+    *reinterpret_cast<u32x4_t *>(&k_s[t][8 * c]) = kv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vt_s[8 * c + 2 * i][t] = static_cast<uint16_t>(vv[i] & 0xffffu);
+      vt_s[8 * c + 2 * i + 1][t] = static_cast<uint16_t>(vv[i] >> 16);
+    }
+  }
+  __syncthreads();
+  {
+    // scores of token t for heads sg + kScoreGroups i
+    const int t = tid % kRingChunk;
+    const int sg = tid / kRingChunk;
+    float dot[kScoreHeads];
+#pragma unroll
+    for (int i = 0; i < kScoreHeads; ++i) dot[i] = 0.0f;
+    for (int c = 0; c < kVec; ++c) {
+      const u32x4_t kw = *reinterpret_cast<const u32x4_t *>(&k_s[t][8 * c]);
+      float kx[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kx[2 * e] = bf16_bits_to_float(kw[e] & 0xffffu);
+        kx[2 * e + 1] = bf16_bits_to_float(kw[e] >> 16);
+      }
+#pragma unroll
+      for (int i = 0; i < kScoreHeads; ++i) {
+        const int g = sg + kScoreGroups * i;
+        if (g < G) {
+          const float4_t qa = *reinterpret_cast<const float4_t *>(&q_s[g][8 * c]);
+          const float4_t qb = *reinterpret_cast<const float4_t *>(&q_s[g][8 * c + 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dot[i] = fmaf(qa[e], kx[e], dot[i]);
+            dot[i] = fmaf(qb[e], kx[4 + e], dot[i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kScoreHeads; ++i) {
+      const int g = sg + kScoreGroups * i;
+      if (g < G) p_s[g][t] = t < n ? dot[i] * p.scale_log2 : -INFINITY;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kScoreHeads; ++i) {
+    const int g = wave + kScoreGroups * i;  // one wave per head, lane = token
+    if (g < G) {
+      const float sc = p_s[g][lane];
+      const float m = wave_max(sc);
+      const float pt = (sc == -INFINITY) ? 0.0f : exp2f(sc - m);
+      p_s[g][lane] = pt;
+      const float l = wave_sum(pt);
+      if (lane == 0) {
+        float *dst = p.partials + ((part0 + g) * p.splits_total + slot) * pstride;
+        dst[0] = m;
+        dst[1] = l;
+      }
+    }
+  }
+  __syncthreads();
+  const int col = tid % D;
+  const int grp = tid / D;
+  if (grp < kHeadGroups) {
+    float acc[kAcc];
+#pragma unroll
+    for (int a = 0; a < kAcc; ++a) acc[a] = 0.0f;
+    for (int t = 0; t < n; t += 8) {
+      const u32x4_t vw = *reinterpret_cast<const u32x4_t *>(&vt_s[col][t]);
+      float vx[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vx[2 * e] = bf16_bits_to_float(vw[e] & 0xffffu);
+        vx[2 * e + 1] = bf16_bits_to_float(vw[e] >> 16);
+      }
+#pragma unroll
+      for (int a = 0; a < kAcc; ++a) {
+        const int g = grp + a * kHeadGroups;
+        if (g < G) {
+          // tokens >= n have p = 0 and zero-filled values
+          const float4_t pa = *reinterpret_cast<const float4_t *>(&p_s[g][t]);
+          const float4_t pb = *reinterpret_cast<const float4_t *>(&p_s[g][t + 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[a] = fmaf(pa[e], vx[e], acc[a]);
+            acc[a] = fmaf(pb[e], vx[4 + e], acc[a]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < kAcc; ++a) {
+      const int g = grp + a * kHeadGroups;
+      if (g < G) p.partials[((part0 + g) * p.splits_total + slot) * pstride + 4 + col] = acc[a];
+    }
+  }
+}
+
+constexpr int kReduceThreads = 256;
+constexpr int kReduceBatch = 4;
+
+// Merge of the split partials of one (sequence, query head): nslots
+// compressed-token partials (+ the ring's). Thread (c, r) owns float4 column
+// c and merges slots r, r + R, ... with a running log-sum-exp (base 2),
+// kReduceBatch slots per step so their loads overlap; the R phases are then
+// merged through LDS.
+template <int D>
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeParams p) {
+  constexpr int kCols = D / 4;                   // float4 columns
+  constexpr int R = kReduceThreads / kCols;      // slot phases
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int j = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int col = tid % kCols;
+  const int r = tid / kCols;
+  const int G = p.num_q_heads / p.num_kv_heads;
   const int ps = partial_stride(D);
-  const float *part = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + hq) * p.splits_total * ps;
   int nslots = 0;
   if (p.max_splits > 0) {
     // the split kernel's work division (header written before this launch)
@@ -765,27 +824,70 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
     const int pb = p.plan[4 + b];
     const int nb = p.plan[4 + b + 1] - pb;
     if (nb > 0) {
-      const int h = hq / (p.num_q_heads / p.num_kv_heads);
-      const long long s0 = static_cast<long long>(pb) * p.num_kv_heads + static_cast<long long>(h) * nb;
+      const long long s0 = static_cast<long long>(pb) * p.num_kv_heads + static_cast<long long>(hq / G) * nb;
       nslots = first_wave(s0 + nb - 1, total, active) - first_wave(s0, total, active) + 1;
     }
   }
-  const bool ring = p.ring_cap > 0;
-  float m = -INFINITY;
-  for (int s = 0; s < nslots; ++s) m = fmaxf(m, part[s * ps]);
-  if (ring) m = fmaxf(m, part[p.max_splits * ps]);
-  float l = 0.0f, o = 0.0f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < nslots + (ring ? 1 : 0); ++s) {
-      const int slot = s < nslots ? s : p.max_splits;
-      const float ms = part[slot * ps];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - m);
-      l = fmaf(part[slot * ps + 1], w, l);
-      o = fmaf(part[slot * ps + 4 + j], w, o);
+  const int n = nslots + (p.splits_total - p.max_splits);  // + ring chunks
+  const float *part = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + hq) * p.splits_total * ps;
+  float m = -INFINITY, l = 0.0f;
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (r < R) {
+    for (int s0 = r; s0 < n; s0 += R * kReduceBatch) {
+      float ms[kReduceBatch], ls[kReduceBatch];
+      float4_t as[kReduceBatch];
+#pragma unroll
+      for (int i = 0; i < kReduceBatch; ++i) {
+        const int s = s0 + i * R;
+        ms[i] = -INFINITY;
+        ls[i] = 0.0f;
+        as[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if (s < n) {
+          const float *e = part + static_cast<int64_t>(s < nslots ? s : p.max_splits + (s - nslots)) * ps;
+          ms[i] = e[0];
+          ls[i] = e[1];
+          as[i] = reinterpret_cast<const float4_t *>(e + kPartStride_pad)[col];
+        }
+      }
+      float mb = m;
+#pragma unroll
+      for (int i = 0; i < kReduceBatch; ++i) mb = fmaxf(mb, ms[i]);
+      if (mb > -INFINITY) {
+        const float a = exp2f(m - mb);
+        acc = acc * a;
+        l = l * a;
+#pragma unroll
+        for (int i = 0; i < kReduceBatch; ++i) {
+          const float w = ms[i] > -INFINITY ? exp2f(ms[i] - mb) : 0.0f;
+          acc = acc + as[i] * w;
+          l = fmaf(ls[i], w, l);
+        }
+        m = mb;
+      }
     }
   }
-  p.out[(static_cast<int64_t>(b) * p.num_q_heads + hq) * D + j] = (l > 0.0f) ? o / l : 0.0f;
+  __shared__ float4_t red_acc[kReduceThreads];
+  __shared__ float red_m[kReduceThreads], red_l[kReduceThreads];
+  red_m[tid] = m;
+  red_l[tid] = l;
+  red_acc[tid] = acc;
+  __syncthreads();
+  if (r == 0) {
+    for (int rr = 1; rr < R; ++rr) {
+      const int t = rr * kCols + col;
+      const float ms = red_m[t];
+      if (ms > -INFINITY) {
+        const float mn = fmaxf(m, ms);
+        const float a = exp2f(m - mn);
+        const float w = exp2f(ms - mn);
+        acc = acc * a + red_acc[t] * w;
+        l = l * a + red_l[t] * w;
+        m = mn;
+      }
+    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    reinterpret_cast<float4_t *>(p.out + (static_cast<int64_t>(b) * p.num_q_heads + hq) * D)[col] = acc * inv;
+  }
 }
 
 // Workgroups of the split kernel that fit on the device at once
@@ -828,11 +930,12 @@ int launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   if (p.ring_cap > 0) {
-    hipLaunchKernelGGL((decode_ring_kernel<D>), dim3(1, p.num_kv_heads, p.batch), dim3(kRingThreads), 0, s, p, qd);
+    const int chunks = (p.ring_cap + kRingChunk - 1) / kRingChunk;
+    hipLaunchKernelGGL((decode_ring_kernel<D>), dim3(p.num_kv_heads, p.batch, chunks), dim3(kRingThreads), 0, s, p, qd);
     const int err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(p.num_q_heads, p.batch), dim3(D), 0, s, p);
+  hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(p.num_q_heads, p.batch), dim3(kReduceThreads), 0, s, p);
   return hipGetLastError();
 }
 

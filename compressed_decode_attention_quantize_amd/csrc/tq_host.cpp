@@ -157,7 +157,7 @@ tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_
   const int min_tokens = split_tokens > 0 ? split_tokens : kMinTokensPerWave;
   plan->split_tokens = split_tokens;
   plan->max_splits = max_seq_len > 0 ? ceil_div_i(max_seq_len, min_tokens) + 1 : 0;
-  plan->splits_total = plan->max_splits + (ring_cap > 0 ? 1 : 0);
+  plan->splits_total = plan->max_splits + (ring_cap + kRingChunk - 1) / kRingChunk;
   plan->header_bytes = ((16 + 4 * (static_cast<size_t>(batch) + 1) + 255) / 256) * 256;
   plan->workspace_bytes = plan->header_bytes + static_cast<size_t>(batch) * num_q_heads *
                                                    std::max(plan->splits_total, 1) * (cfg.head_dim + 4) *

@@ -163,8 +163,9 @@ tq_status tq_quantize_append(const tq_config *cfg, int layer_idx,
  * is balanced whatever the mix of lengths. The workspace holds a header
  * (16 + 4 (batch + 1) bytes, rounded up to 256) and one fp32 partial
  * (max, sum, acc[head_dim]) per (sequence, query head, slot) with
- * ceil(max_seq_len / min tokens) + 1 slots, plus one for the ring when
- * ring_cap > 0. num_splits_out (nullable) receives the slots per sequence.
+ * ceil(max_seq_len / min tokens) + 1 slots, plus one per 64 ring tokens
+ * (ceil(ring_cap / 64)). num_splits_out (nullable) receives the slots per
+ * sequence.
  */
 tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, int num_q_heads,
                                    int max_seq_len, int ring_cap, int split_tokens,
@@ -190,11 +191,12 @@ tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, int num_q_he
  *  seq_lens      device int32 [batch], compressed tokens per sequence; must
  *                be <= max_seq_len (the host hint used to size the splits);
  *                tokens beyond it are ignored.
- *  ring_k/ring_v device bf16 [batch][num_kv_heads][ring_cap][head_dim], or
+ *  ring_k/ring_v device bf16 [batch][num_kv_heads][ring_cap][head_dim],
+ *                16-byte aligned, or
  *                NULL (then ring_lens is ignored and ring_cap must be 0);
  *                ring_lens device int32 [batch], clamped to ring_cap.
  *  softmax_scale <= 0 means 1/sqrt(head_dim).
- *  out           device fp32 [batch][num_q_heads][head_dim].
+ *  out           device fp32 [batch][num_q_heads][head_dim], 16-byte aligned.
  *  workspace     device, at least tq_decode_workspace_size bytes, 16-byte
  *                aligned; its contents on entry do not matter.
  *  block_size    a multiple of 16.
