@@ -288,22 +288,49 @@ __device__ __forceinline__ void key_operand(const uint32_t *words, uint32_t off,
   }
 }
 
+// Hand-off of LDS data between lanes of one wave: lanes write, other lanes
+// of the same wave read. The hardware keeps one wave's LDS operations in
+// order; the fence tells the compiler that other lanes' stores are visible
+// here, so it neither forwards a lane's own earlier values to the reads nor
+// moves memory accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+// Reductions over the 4 lane rows of an MFMA column (lanes c, c + 16,
+// c + 32, c + 48) with the gfx950 row-swap permutes: swapping a register
+// with itself gives both halves of each row pair.
+__device__ __forceinline__ float column_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float column_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // 16-bit field at an even byte offset of an LDS word array.
 __device__ __forceinline__ uint32_t lds_u16(const uint32_t *words, uint32_t off) {
   const uint32_t w = words[off >> 2];
   return (off & 2u) ? (w >> 16) : (w & 0xffffu);
 }
 
-template <int D, int KB, int VB>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D == 96 ? 2 : 3))) void decode_split_kernel(DecodeParams p, int q_dtype) {
+// NB = tiles per macro tile: the 16 MFMA columns hold NB tile slots of
+// GP = 16 / NB query heads each (NB = 4 for G <= 4, 2 for G <= 8, 1 else).
+template <int D, int KB, int VB, int NB>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(DecodeParams p, int q_dtype) {
   using GE = Geo<D, KB, VB>;
   using VX = ValueExpand<VB>;
   constexpr int S = GE::kSlot;
   constexpr int KM = GE::kKM;
+  constexpr int GP = 16 / NB;
 
   __shared__ uint32_t lut[GE::kLut];
   __shared__ __align__(16) uint32_t scratch[kWaves][GE::kScratch / 4];
-  __shared__ __align__(16) float tok[kWaves][3][16];
+  // per-token scalars of the macro tile: norm * scale (< 0: masked), s', z' + c0 s', ||c||^2
+  __shared__ __align__(16) float tokf[kWaves][4][NB][16];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -393,54 +420,60 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D =
 
   uint32_t *scr = scratch[wave];  // this wave's LDS: queries, then the staged tile
 
-  // ---- rotated queries as f16 hi + lo parts, in the MFMA B-operand layout
+  // ---- rotated queries as f16 hi + lo parts, in the MFMA B-operand layout.
+  // Column n of the score MFMA is query head n % GP of tile slot n / GP:
+  // every tile slot sees the same GP query heads (heads >= G are zero).
   half8_t qf[KM], ql[KM];
   {
     using T = Team<D>;
     const int team = lane / T::kLanes;
     const int r = lane - team * T::kLanes;
     constexpr int rows_per_pass = T::kPerWave;
-    constexpr int kPasses = (16 + rows_per_pass - 1) / rows_per_pass;
+    constexpr int kPasses = (GP + rows_per_pass - 1) / rows_per_pass;
     u32x4_t qhi[kPasses], qlo[kPasses];
-    for (int g0 = 0; g0 < 16; g0 += rows_per_pass) {
-      const int g = g0 + team;
+#pragma unroll
+    for (int k = 0; k < kPasses; ++k) {
+      const int g = k * rows_per_pass + team;
       float x[8];
       const bool live = team < rows_per_pass && g < G;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        x[i] = live ? load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + 8 * r + i)
+      for (int e = 0; e < 8; ++e)
+        x[e] = live ? load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + 8 * r + e)
                     : 0.0f;
       if constexpr (GE::kMse) {
         const uint32_t sb = lane_sign_bits(p.sign_words, r);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = flip_sign(x[i], (sb >> i) & 1u);
+        for (int e = 0; e < 8; ++e) x[e] = flip_sign(x[e], (sb >> e) & 1u);
         team_wht<D>(x, r % T::kBlockLanes);
         const float rb = rsqrtf(static_cast<float>(T::kBlock));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] *= rb;
+        for (int e = 0; e < 8; ++e) x[e] *= rb;
       }
-      if (team < rows_per_pass && g < 16) {
-        u32x4_t hv, lv;
+      u32x4_t hv, lv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hv[i] = f16_pair_bits(x[2 * i], x[2 * i + 1]);
-          const float h0 = f16_bits_to_float(hv[i] & 0xffffu), h1 = f16_bits_to_float(hv[i] >> 16);
-          lv[i] = f16_pair_bits(x[2 * i] - h0, x[2 * i + 1] - h1);
-        }
-        qhi[g0 / rows_per_pass] = hv;
-        qlo[g0 / rows_per_pass] = lv;
+      for (int e = 0; e < 4; ++e) {
+        hv[e] = f16_pair_bits(x[2 * e], x[2 * e + 1]);
+        const float h0 = f16_bits_to_float(hv[e] & 0xffffu), h1 = f16_bits_to_float(hv[e] >> 16);
+        lv[e] = f16_pair_bits(x[2 * e] - h0, x[2 * e + 1] - h1);
       }
+      qhi[k] = hv;
+      qlo[k] = lv;
     }
     // hi parts through LDS into the MFMA operand layout, then the lo parts
     _Float16 *qs = reinterpret_cast<_Float16 *>(scr);
 #pragma unroll
     for (int phase = 0; phase < 2; ++phase) {
+      wave_lds_sync();  // earlier reads of this plane (other lanes) are done
 #pragma unroll
       for (int k = 0; k < kPasses; ++k) {
         const int g = k * rows_per_pass + team;
-        if (team < rows_per_pass && g < 16)
-          *reinterpret_cast<u32x4_t *>(qs + g * D + 8 * r) = phase == 0 ? qhi[k] : qlo[k];
+        if (team < rows_per_pass && g < GP) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            *reinterpret_cast<u32x4_t *>(qs + (j * GP + g) * D + 8 * r) = phase == 0 ? qhi[k] : qlo[k];
+        }
       }
+      wave_lds_sync();  // the rows other lanes wrote are visible
 #pragma unroll
       for (int m = 0; m < KM; ++m) {
         const half8_t v = *reinterpret_cast<const half8_t *>(qs + col * D + kq * (D / 4) + 8 * m);
@@ -450,11 +483,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D =
     }
   }
 
-  // ---- tile loop
+  // ---- macro-tile loop: NB tiles of 16 tokens, tile i in column group i
   float4_t acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_lane = 0.0f, z_lane = 0.0f;
+  const int my_tile = col / GP;  // tile slot of this lane's column
 
   // Tiles go HBM -> LDS by direct loads (global_load_lds_dwordx4: lane l of
   // a load instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS window),
@@ -462,7 +496,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D =
   constexpr int kLoads = GE::kChunksPerLane;     // load instructions per tile
   // Block ids of the segment, 64 at a time: lane i holds the id of logical
   // block blk_base + i; tiles pick theirs with readlane.
-  int blk_base = -1 << 30, blk_lane = 0;
+  int blk_base = -(1 << 30), blk_lane = 0;
   bool ok_next = false;
   auto issue = [&](int tile0, int bsel) {
     const int lblk = tile0 / p.block_size;
@@ -489,73 +523,95 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D =
       if (c < GE::kTileChunks) load_lds_16(src + 16 * c, dst + 1024 * k);
     }
   };
+  wave_lds_sync();  // the query plane reads are done before tile loads overwrite it
   issue(begin, 0);
 
   const float c0 = static_cast<float>(VX::kC0);
   const float inv_sigma = 1.0f / p.centroid_scale;
+  const bool nc = GE::kMse && p.norm_correction;
   int bsel = 0;
-  for (int tile0 = begin; tile0 < end; tile0 += kTile, bsel ^= 1) {
-    const int ntok = min(kTile, end - tile0);
-    const bool tile_ok = ok_next;
-    if (tile0 + kTile < end) {
-      issue(tile0 + kTile, bsel ^ 1);
-      wait_vmcnt<kLoads>();  // this tile's loads are done, the next tile's may run
-    } else {
-      wait_vmcnt<0>();
-    }
-    const uint32_t *tw = scr + bsel * (GE::kTileBuf / 4);  // this tile's bytes as words
-
-    // per-token scalars: lane t < 16 reads its slot's norm / scale / zero
-    if (lane < 16) {
-      const uint32_t slot = static_cast<uint32_t>(lane * S);
-      const bool ok = tile_ok && lane < ntok;
-      float fb = p.scale_log2;
-      if constexpr (GE::kMse) fb *= f16_bits_to_float(lds_u16(tw, slot + GE::kKeyCodeBytes));
-      const float s1 = f16_bits_to_float(lds_u16(tw, slot + GE::kKeyBytes + GE::kValCodeBytes));
-      const float z1 = f16_bits_to_float(lds_u16(tw, slot + GE::kKeyBytes + GE::kValCodeBytes + 2));
-      tok[wave][0][lane] = ok ? fb : -1.0f;  // negative marks a masked token
-      tok[wave][1][lane] = ok ? s1 : 0.0f;
-      tok[wave][2][lane] = ok ? fmaf(c0, s1, z1) : 0.0f;
-    }
-
-    // keys -> scores S^T[4kq + r][col]
-    half8_t kf[KM];
-    key_operand<D, KB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
-    float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int mt0 = begin; mt0 < end; mt0 += NB * kTile) {
+    uint32_t vraw[NB][4];
+    float4_t sraw = {0.0f, 0.0f, 0.0f, 0.0f};
+    // ---- phase A, per tile: scores into the tile's column group, value
+    // code words kept in registers, per-token scalars to LDS
 #pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[m], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], ql[m], sc, 0, 0, 0);
-    }
-    float4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (GE::kMse) {
-      if (p.norm_correction) {
-#pragma unroll
-        for (int m = 0; m < KM; ++m) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], kf[m], gram, 0, 0, 0);
-      }
-    }
+    for (int i = 0; i < NB; ++i) {
+      const int tile0 = mt0 + i * kTile;
+      if (tile0 < end) {
+        const int ntok = min(kTile, end - tile0);
+        const bool tile_ok = ok_next;
+        if (tile0 + kTile < end) {
+          issue(tile0 + kTile, bsel ^ 1);
+          wait_vmcnt<kLoads>();  // this tile's loads are done, the next tile's may run
+        } else {
+          wait_vmcnt<0>();
+        }
+        const uint32_t *tw = scr + bsel * (GE::kTileBuf / 4);  // this tile's bytes as words
+        bsel ^= 1;
 
-    // value codes of element group col for tokens 4kq..4kq+3
-    half4_t av[8];
-    {
-      uint32_t d[4];
-      if (col < GE::kGroups) {
+        // per-token scalars: lane t < 16 reads its slot's norm / scale / zero
+        if (lane < 16) {
+          const uint32_t slot = static_cast<uint32_t>(lane * S);
+          const bool ok = tile_ok && lane < ntok;
+          float fb = p.scale_log2;
+          if constexpr (GE::kMse) fb *= f16_bits_to_float(lds_u16(tw, slot + GE::kKeyCodeBytes));
+          const float s1 = f16_bits_to_float(lds_u16(tw, slot + GE::kKeyBytes + GE::kValCodeBytes));
+          const float z1 = f16_bits_to_float(lds_u16(tw, slot + GE::kKeyBytes + GE::kValCodeBytes + 2));
+          tokf[wave][0][i][lane] = ok ? fb : -1.0f;  // negative marks a masked token
+          tokf[wave][1][i][lane] = ok ? s1 : 0.0f;
+          tokf[wave][2][i][lane] = ok ? fmaf(c0, s1, z1) : 0.0f;
+        }
+
+        // keys -> scores S^T[4kq + r][col]; this lane keeps them if col is in
+        // the tile's column group
+        half8_t kf[KM];
+        key_operand<D, KB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
+        float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const auto w = lds_bytes<VB>(tw, static_cast<uint32_t>((4 * kq + r) * S + GE::kKeyBytes + VB * col));
-          d[r] = w.w[0];
+        for (int m = 0; m < KM; ++m) {
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[m], sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], ql[m], sc, 0, 0, 0);
+        }
+        if (my_tile == i) sraw = sc;
+        if constexpr (GE::kMse) {
+          if (nc) {
+            // ||c_t||^2 of token t = 4kq + r sits on the Gram diagonal, at
+            // lane (kq, col = t), register r
+            float4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int m = 0; m < KM; ++m) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], kf[m], gram, 0, 0, 0);
+            const int rr = col - 4 * kq;
+            const float dg = rr == 0 ? gram[0] : rr == 1 ? gram[1] : rr == 2 ? gram[2] : gram[3];
+            if (rr >= 0 && rr < 4) tokf[wave][3][i][col] = dg;
+          }
+        }
+
+        // value codes of element group col for tokens 4kq..4kq+3
+        if (col < GE::kGroups) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            vraw[i][r] = lds_bytes<VB>(tw, static_cast<uint32_t>((4 * kq + r) * S + GE::kKeyBytes + VB * col)).w[0];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vraw[i][r] = 0u;
         }
       } else {
+        // tile slot past the end of the segment: all its tokens masked
+        if (lane < 16) tokf[wave][0][i][lane] = -1.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) d[r] = 0u;
+        for (int r = 0; r < 4; ++r) vraw[i][r] = 0u;
       }
-      VX::run(d, av);  // rows col >= kGroups are padding and never written out
     }
 
-    const float4_t fb4 = *reinterpret_cast<const float4_t *>(&tok[wave][0][4 * kq]);
-    const float4_t s14 = *reinterpret_cast<const float4_t *>(&tok[wave][1][4 * kq]);
-    const float4_t zc4 = *reinterpret_cast<const float4_t *>(&tok[wave][2][4 * kq]);
-
+    // ---- phase B, once per macro tile: lane (kq, col) holds tokens
+    // 4kq..4kq+3 of tile my_tile for query head col % GP
+    wave_lds_sync();  // per-token scalars written by other lanes
+    const float4_t fb4 = *reinterpret_cast<const float4_t *>(&tokf[wave][0][my_tile][4 * kq]);
+    const float4_t s14 = *reinterpret_cast<const float4_t *>(&tokf[wave][1][my_tile][4 * kq]);
+    const float4_t zc4 = *reinterpret_cast<const float4_t *>(&tokf[wave][2][my_tile][4 * kq]);
+    float4_t nn4 = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (nc) nn4 = *reinterpret_cast<const float4_t *>(&tokf[wave][3][my_tile][4 * kq]);
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -563,19 +619,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D =
       if constexpr (GE::kMse) {
         // centroids carry the table scale sigma: it cancels under norm
         // correction and is divided out otherwise
-        if (p.norm_correction) {
-          const float nn = __shfl(gram[r], 20 * kq + r, 64);
-          f = f * rsqrtf(nn);
-        } else {
-          f = f * inv_sigma;
-        }
+        f *= nc ? __builtin_amdgcn_rsqf(nn4[r]) : inv_sigma;
       }
-      s[r] = (fb4[r] >= 0.0f) ? sc[r] * f : -INFINITY;
+      s[r] = (fb4[r] >= 0.0f) ? sraw[r] * f : -INFINITY;
     }
-    // running max over the tile: 4 registers, then the 4 lane groups
-    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    // running max of the column: 4 registers, then the 4 lane rows
+    const float mt = column_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
     if (mt > m_run) {
       const float alpha = exp2f(m_run - mt);
 #pragma unroll
@@ -585,38 +634,73 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D =
       m_run = mt;
     }
     const float mr = (m_run == -INFINITY) ? 0.0f : m_run;
-    float pr[4];
+    float w[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pr[r] = __builtin_amdgcn_exp2f(s[r] - mr);
-      l_lane += pr[r];
-      z_lane = fmaf(pr[r], zc4[r], z_lane);
+      const float pr = __builtin_amdgcn_exp2f(s[r] - mr);
+      l_lane += pr;
+      z_lane = fmaf(pr, zc4[r], z_lane);
+      w[r] = pr * s14[r];
     }
     // weights p * s' as f16 hi + lo parts: the value contraction then sees
     // them to ~22 bits (f16 alone leaves a 2^-12 error that cancellation in
     // the weighted sum can amplify)
-    float w[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = pr[r] * s14[r];
     u32x2_t hw, lw;
     hw[0] = f16_pair_bits(w[0], w[1]);
     hw[1] = f16_pair_bits(w[2], w[3]);
     lw[0] = f16_pair_bits(w[0] - f16_bits_to_float(hw[0] & 0xffffu), w[1] - f16_bits_to_float(hw[0] >> 16));
     lw[1] = f16_pair_bits(w[2] - f16_bits_to_float(hw[1] & 0xffffu), w[3] - f16_bits_to_float(hw[1] >> 16));
-    const half4_t pvh = __builtin_bit_cast(half4_t, hw);
-    const half4_t pvl = __builtin_bit_cast(half4_t, lw);
+    wave_lds_sync();  // scalar reads done before the next macro tile rewrites them
+
+    // ---- phase C, per tile: value MFMAs with the weights of the tile's
+    // column group only (zero elsewhere)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[c], pvh, acc[c], 0, 0, 0);
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[c], pvl, acc[c], 0, 0, 0);
+    for (int i = 0; i < NB; ++i) {
+      if (mt0 + i * kTile < end) {
+        const bool mine = my_tile == i;
+        u32x2_t bh, bl;
+        bh[0] = mine ? hw[0] : 0u;
+        bh[1] = mine ? hw[1] : 0u;
+        bl[0] = mine ? lw[0] : 0u;
+        bl[1] = mine ? lw[1] : 0u;
+        const half4_t pvh = __builtin_bit_cast(half4_t, bh);
+        const half4_t pvl = __builtin_bit_cast(half4_t, bl);
+        half4_t av[8];
+        VX::run(vraw[i], av);  // rows col >= kGroups are padding and never written out
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[c], pvh, acc[c], 0, 0, 0);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[c], pvl, acc[c], 0, 0, 0);
+        }
+      }
     }
   }
 
   // ---- partial (m, l, acc + zero terms) of query head col
-  l_lane += __shfl_xor(l_lane, 16, 64);
-  l_lane += __shfl_xor(l_lane, 32, 64);
-  z_lane += __shfl_xor(z_lane, 16, 64);
-  z_lane += __shfl_xor(z_lane, 32, 64);
+  l_lane = column_sum(l_lane);
+  z_lane = column_sum(z_lane);
+  if constexpr (NB > 1) {
+    // merge the NB tile slots of each query head: lanes col, col + GP, ...
+    // of the same 16-lane row
+    float mm = m_run;
+#pragma unroll
+    for (int o = GP; o < 16; o <<= 1) mm = fmaxf(mm, __shfl_xor(mm, o, 64));
+    const float a = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - mm);
+    l_lane *= a;
+    z_lane *= a;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] *= a;
+#pragma unroll
+    for (int o = GP; o < 16; o <<= 1) {
+      l_lane += __shfl_xor(l_lane, o, 64);
+      z_lane += __shfl_xor(z_lane, o, 64);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], o, 64);
+    }
+    m_run = mm;
+  }
   if (col < G) {
     float *dst = part_base + static_cast<int64_t>(col) * p.splits_total * pstride;
     if (kq == 0) {
@@ -912,20 +996,20 @@ int resident_workgroups(const void *kernel, size_t dyn_lds) {
   return n;
 }
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, int NB>
 int launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   const int qd = static_cast<int>(q_dtype);
   if (p.max_splits > 0) {
     const size_t dyn = static_cast<size_t>(p.batch + 1) * sizeof(int32_t);
-    const void *kern = reinterpret_cast<const void *>(&decode_split_kernel<D, KB, VB>);
+    const void *kern = reinterpret_cast<const void *>(&decode_split_kernel<D, KB, VB, NB>);
     const int resident = resident_workgroups(kern, dyn);
     if (resident < 0) return hipErrorInvalidValue;
     // enough waves for the largest possible context, capped at what fits
     const long long worst_tiles = static_cast<long long>(p.batch) * p.num_kv_heads * ((p.max_seq_len + kTile - 1) / kTile);
     const long long need = (work_waves(worst_tiles, 1 << 30, p.split_tokens) + kWaves - 1) / kWaves;
     const int grid = static_cast<int>(std::max(1LL, std::min<long long>(need, resident)));
-    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB>), dim3(grid), dim3(64 * kWaves), dyn, s, p, qd);
+    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, NB>), dim3(grid), dim3(64 * kWaves), dyn, s, p, qd);
     const int err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -939,15 +1023,23 @@ int launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int KB, int VB>
+int dispatch_decode_group(tq_dtype qd, const DecodeParams &p, hipStream_t s) {
+  const int G = p.num_q_heads / p.num_kv_heads;
+  if (G <= 4) return launch_decode_t<D, KB, VB, 4>(qd, p, s);
+  if (G <= 8) return launch_decode_t<D, KB, VB, 2>(qd, p, s);
+  return launch_decode_t<D, KB, VB, 1>(qd, p, s);
+}
+
 template <int D>
 int dispatch_decode_bits(const tq_config &c, tq_dtype qd, const DecodeParams &p, hipStream_t s) {
   const int kb = c.key_quant_bits, vb = c.value_quant_bits;
-  if (kb == 3 && vb == 3) return launch_decode_t<D, 3, 3>(qd, p, s);
-  if (kb == 3 && vb == 4) return launch_decode_t<D, 3, 4>(qd, p, s);
-  if (kb == 4 && vb == 3) return launch_decode_t<D, 4, 3>(qd, p, s);
-  if (kb == 4 && vb == 4) return launch_decode_t<D, 4, 4>(qd, p, s);
-  if (kb == 8 && vb == 3) return launch_decode_t<D, 8, 3>(qd, p, s);
-  if (kb == 8 && vb == 4) return launch_decode_t<D, 8, 4>(qd, p, s);
+  if (kb == 3 && vb == 3) return dispatch_decode_group<D, 3, 3>(qd, p, s);
+  if (kb == 3 && vb == 4) return dispatch_decode_group<D, 3, 4>(qd, p, s);
+  if (kb == 4 && vb == 3) return dispatch_decode_group<D, 4, 3>(qd, p, s);
+  if (kb == 4 && vb == 4) return dispatch_decode_group<D, 4, 4>(qd, p, s);
+  if (kb == 8 && vb == 3) return dispatch_decode_group<D, 8, 3>(qd, p, s);
+  if (kb == 8 && vb == 4) return dispatch_decode_group<D, 8, 4>(qd, p, s);
   return hipErrorInvalidValue;
 }
 
