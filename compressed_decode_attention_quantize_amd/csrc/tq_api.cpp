@@ -123,8 +123,8 @@ TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, con
   if (batch == 0) return TQ_OK;
   if (!q || !kv_pool || !block_tables || !seq_lens || !out)
     return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: NULL pointer");
-  if (!aligned16(kv_pool) || !aligned16(out) || (has_ring && (!aligned16(ring_k) || !aligned16(ring_v))))
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: kv_pool, out, ring_k and ring_v must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || (has_ring && (!aligned16(ring_k) || !aligned16(ring_v))))
+    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: q, kv_pool, out, ring_k and ring_v must be 16-byte aligned");
   SplitPlan plan;
   st = plan_decode(*cfg, batch, num_q_heads, max_seq_len, ring_cap, split_tokens, &plan);
   if (st != TQ_OK) return st;

@@ -411,10 +411,15 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   const long long seg_stop = seg_start + nb;
   const long long run_end = seg_stop < f_end ? seg_stop : f_end;
   const int slot = w - first_wave(seg_start, total, active);
-  const int len = min(max(p.seq_lens[b], 0), seq_cap);
   const int begin = static_cast<int>(f - seg_start) * kTile;
-  const int end = min(len, static_cast<int>(run_end - seg_start) * kTile);
-  f = run_end;
+  // The range's first loads go out together: its length, the block ids of
+  // its first 64 blocks (lane i: logical block blk_base + i) and, below, the
+  // query rows.
+  const int len_raw = p.seq_lens[b];
+  int blk_base = begin / p.block_size;
+  int blk_lane = blk_base + lane < p.max_blocks_per_seq
+                     ? p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + blk_base + lane]
+                     : 0;
   float *part_base = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + h * G) * p.splits_total * pstride +
                      static_cast<int64_t>(slot) * pstride;
 
@@ -431,15 +436,44 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     constexpr int rows_per_pass = T::kPerWave;
     constexpr int kPasses = (GP + rows_per_pass - 1) / rows_per_pass;
     u32x4_t qhi[kPasses], qlo[kPasses];
+    // raw query rows first (16 or 32 bytes per lane; lanes without a live
+    // head read head 0 and discard it), so all loads are in flight at once
+    u32x4_t qraw[kPasses][2];
+#pragma unroll
+    for (int k = 0; k < kPasses; ++k) {
+      const int g = k * rows_per_pass + team;
+      const bool live = team < rows_per_pass && g < G;
+      const int64_t e0 = (static_cast<int64_t>(b) * p.num_q_heads + h * G + (live ? g : 0)) * D + 8 * r;
+      if (q_dtype == TQ_F32) {
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const float *>(p.q) + e0);
+        qraw[k][0] = src[0];
+        qraw[k][1] = src[1];
+      } else {
+        qraw[k][0] = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p.q) + e0);
+        qraw[k][1] = qraw[k][0];
+      }
+    }
 #pragma unroll
     for (int k = 0; k < kPasses; ++k) {
       const int g = k * rows_per_pass + team;
       float x[8];
       const bool live = team < rows_per_pass && g < G;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[e] = live ? load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + 8 * r + e)
-                    : 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w0 = qraw[k][0][e];
+        if (q_dtype == TQ_F32) {
+          x[e] = __uint_as_float(w0);
+          x[4 + e] = __uint_as_float(qraw[k][1][e]);
+        } else if (q_dtype == TQ_BF16) {
+          x[2 * e] = bf16_bits_to_float(w0 & 0xffffu);
+          x[2 * e + 1] = bf16_bits_to_float(w0 >> 16);
+        } else {
+          x[2 * e] = f16_bits_to_float(w0 & 0xffffu);
+          x[2 * e + 1] = f16_bits_to_float(w0 >> 16);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = live ? x[e] : 0.0f;
       if constexpr (GE::kMse) {
         const uint32_t sb = lane_sign_bits(p.sign_words, r);
 #pragma unroll
@@ -483,6 +517,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     }
   }
 
+  const int len = min(max(len_raw, 0), seq_cap);
+  const int end = min(len, static_cast<int>(run_end - seg_start) * kTile);
+  f = run_end;
+
   // ---- macro-tile loop: NB tiles of 16 tokens, tile i in column group i
   float4_t acc[8];
 #pragma unroll
@@ -494,9 +532,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   // a load instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS window),
   // double buffered: the next tile is in flight while this one is used.
   constexpr int kLoads = GE::kChunksPerLane;     // load instructions per tile
-  // Block ids of the segment, 64 at a time: lane i holds the id of logical
-  // block blk_base + i; tiles pick theirs with readlane.
-  int blk_base = -(1 << 30), blk_lane = 0;
+  // Block ids of the range, 64 at a time (blk_base, blk_lane above); tiles
+  // pick theirs with readlane.
   bool ok_next = false;
   auto issue = [&](int tile0, int bsel) {
     const int lblk = tile0 / p.block_size;
@@ -506,8 +543,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       // refill the window; the wait for this load stays on this branch
       blk_base = lblk;
       const int bi = blk_base + lane;
-      const int last = (end - 1) / p.block_size;
-      blk_lane = bi <= last ? p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + bi] : 0;
+      blk_lane = bi < p.max_blocks_per_seq ? p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + bi] : 0;
       phys = __builtin_amdgcn_readlane(blk_lane, 0);
     } else {
       phys = __builtin_amdgcn_readlane(blk_lane, lblk - blk_base);

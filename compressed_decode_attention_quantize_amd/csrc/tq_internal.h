@@ -99,7 +99,7 @@ int launch_decode(const tq_config &cfg, tq_dtype q_dtype, const DecodeParams &p,
 // Split plan shared by tq_decode_workspace_size and tq_decode_attention.
 struct SplitPlan {
   int32_t split_tokens;   // as given (0 = 256 tokens per wave at least)
-  int32_t max_splits;     // partial slots per (sequence, q head): ceil(max_seq_len / min tokens) + 1
+  int32_t max_splits;     // partial slots per (sequence, q head) for compressed tokens
   int32_t splits_total;   // max_splits + one slot per 64 ring tokens
   size_t header_bytes;    // work-division header (16 + 4 (batch + 1), rounded to 256)
   size_t workspace_bytes; // header + partials

@@ -185,7 +185,7 @@ tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, int num_q_he
  * A sequence with no tokens outputs zeros.
  *
  *  q             device [batch][num_q_heads][head_dim], dtype q_dtype
- *                (F32, BF16 or F16), contiguous.
+ *                (F32, BF16 or F16), contiguous, 16-byte aligned.
  *  kv_pool       device, as written by tq_quantize_append; 16-byte aligned.
  *  block_tables  device int32 [batch][max_blocks_per_seq].
  *  seq_lens      device int32 [batch], compressed tokens per sequence; must
