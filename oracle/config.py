@@ -11,12 +11,20 @@ Pins: slot sizes against the sizes the printed formulas give at head_dim 128
 and the two compression ratios of the docstring that agree with them (2.6x,
 3.8x); preset fields against the docstring's preset descriptions; the error
 text against ``from_cache_dtype``'s message. See tests/test_oracle_config.py.
+
+Bit-width variants: the article on the TurboQuant project's full_tq mode
+(section on the next directions, directions 2 and 3) describes 2-bit values
+(its value quantizer switches between 2 and 4 bits) and layer-adaptive key bits
+(an ``initial_layers_key_bits`` hook parameter that gives the first four layers
+one more key bit). The printed size formulas take any bit width, so a 2-bit
+value field is ceil(D * 2 / 8) + 4 bytes; ``layer_config`` gives the per-layer
+config. Pins: slot sizes by the printed formulas, the layer rule by cases.
 """
 
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 
 # Preset names and their fields, in the order the class docstring lists them.
 # The docstring describes each preset in words: k8v4 = FP8 keys + 4-bit values;
@@ -126,3 +134,26 @@ def layer_seed(seed: int, layer_idx: int) -> int:
     """Per-layer seed: base seed plus 1337 times the layer index (``seed``
     argument description in the class docstring), taken modulo 2**64."""
     return (seed + layer_idx * 1337) % (1 << 64)
+
+
+# Layer-adaptive key bits (article on the TurboQuant project's full_tq mode,
+# direction 3): layers below INITIAL_LAYERS use ``initial_layers_key_bits``
+# key bits. Readings: the parameter is the key bit width of those layers and
+# defaults to one more than the base width; FP8 keys (8) have no wider MSE
+# form, so an FP8 base keeps its keys unless a width is given; everything else
+# (value bits, norm correction, base seed) is the base config's. The layer's
+# seed still comes from layer_seed(seed, layer_idx).
+INITIAL_LAYERS = 4
+
+
+def layer_config(base: TQConfig, layer_idx: int, initial_layers: int = INITIAL_LAYERS,
+                 initial_layers_key_bits: int | None = None) -> TQConfig:
+    if layer_idx < 0 or initial_layers < 0:
+        raise ValueError("layer_idx and initial_layers must be >= 0")
+    if layer_idx >= initial_layers:
+        return base
+    if initial_layers_key_bits is None:
+        if base.key_fp8:
+            return base
+        initial_layers_key_bits = base.key_quant_bits + 1
+    return replace(base, key_quant_bits=initial_layers_key_bits)

@@ -20,7 +20,7 @@ half is its mirror, so the table is exactly antisymmetric. float64 throughout;
 the fp32 table is the rounding of the float64 one, and each fp32 midpoint is
 the rounding of the float64 mean of two adjacent float64 centroids.
 
-Pins: Max's published table for N(0,1) at 8 and 16 levels (tests/golden);
+Pins: Max's published table for N(0,1) at 4, 8 and 16 levels (tests/golden);
 the centroid and midpoint conditions checked with scipy quadrature; the
 distortion against Max's published mean-squared errors.
 """

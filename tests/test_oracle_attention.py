@@ -60,9 +60,13 @@ def _brute(q, pool, tables, lens, cfg, layer, scale):
     return out
 
 
-@pytest.mark.parametrize("preset,d", [("turboquant_3bit_nc", 64), ("turboquant_k8v4", 64), ("turboquant_k3v4_nc", 96)])
+@pytest.mark.parametrize("preset,d", [("turboquant_3bit_nc", 64), ("turboquant_k8v4", 64), ("turboquant_k3v4_nc", 96),
+                                      ((3, 2), 128), ((8, 2), 64)])
 def test_brute_force_tiny(preset, d):
-    cfg = C.from_cache_dtype(preset, d)
+    if isinstance(preset, tuple):  # 2-bit values
+        cfg = C.TQConfig(head_dim=d, key_quant_bits=preset[0], value_quant_bits=preset[1], norm_correction=True)
+    else:
+        cfg = C.from_cache_dtype(preset, d)
     lens = [0, 5, 21]
     pool, tables = _fill(cfg, lens, hkv=2, seed=1)
     q = np.random.default_rng(2).standard_normal((3, 4, d)).astype(np.float32)

@@ -29,7 +29,7 @@ def test_pack_worked_examples():
         assert np.array_equal(back, codes)
 
 
-@pytest.mark.parametrize("bits,d", [(3, 128), (4, 128), (3, 96), (4, 64), (3, 64)])
+@pytest.mark.parametrize("bits,d", [(3, 128), (4, 128), (3, 96), (4, 64), (3, 64), (2, 128), (2, 96)])
 def test_pack_round_trip_and_size(bits, d):
     rng = np.random.default_rng(bits * 1000 + d)
     codes = rng.integers(0, 2 ** bits, size=(50, d), dtype=np.uint8)
@@ -79,7 +79,7 @@ def test_fp8_specials_and_saturation():
 
 # ---------------------------------------------------------------- values
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_value_constant_vector(bits):
     v = np.full((3, 64), 0.7, dtype=np.float32)
     codes, s16, z16 = X.encode_values(v, bits)
@@ -91,7 +91,7 @@ def test_value_constant_vector(bits):
     assert np.array_equal(vhat, np.full((3, 64), np.float32(np.float16(0.7))))
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_value_integer_ramp(bits):
     levels = 2 ** bits - 1
     ramp = np.tile(np.arange(levels + 1, dtype=np.float32), 8)[None, :]
@@ -100,7 +100,7 @@ def test_value_integer_ramp(bits):
     assert np.array_equal(codes[0], ramp[0].astype(np.uint8))
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_value_error_bound(bits):
     rng = np.random.default_rng(bits)
     v = (rng.standard_normal((400, 128)) * rng.uniform(0.01, 20, (400, 1))).astype(np.float32)
@@ -205,6 +205,22 @@ def test_fp8_slot_layout():
     assert np.array_equal(slots[:, 128:192], X.pack_bits(codes, 4))
     assert np.array_equal(slots[:, 192] | (slots[:, 193].astype(np.uint16) << 8), s16)
     assert np.array_equal(slots[:, 194] | (slots[:, 195].astype(np.uint16) << 8), z16)
+
+
+def test_two_bit_value_slot_layout():
+    cfg = C.TQConfig(head_dim=128, key_quant_bits=3, value_quant_bits=2, norm_correction=True)
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((10, 128)).astype(np.float32)
+    v = rng.standard_normal((10, 128)).astype(np.float32)
+    slots = X.encode_slots(k, v, cfg, 2)
+    assert slots.shape == (10, 86)
+    idx, norm16 = X.encode_keys_mse(k, cfg, 2)
+    assert np.array_equal(slots[:, :48], X.pack_bits(idx, 3))
+    codes, s16, z16 = X.encode_values(v, 2)
+    assert codes.max() <= 3
+    assert np.array_equal(slots[:, 50:82], X.pack_bits(codes, 2))
+    assert np.array_equal(slots[:, 82] | (slots[:, 83].astype(np.uint16) << 8), s16)
+    assert np.array_equal(slots[:, 84] | (slots[:, 85].astype(np.uint16) << 8), z16)
 
 
 @pytest.mark.parametrize("preset,d", [("turboquant_4bit_nc", 128), ("turboquant_3bit_nc", 128),

@@ -81,3 +81,41 @@ def test_wht_block():
     assert C.TQConfig(head_dim=128).wht_block == 128
     assert C.TQConfig(head_dim=96).wht_block == 32
     assert C.TQConfig(head_dim=64).wht_block == 64
+
+
+# ---------------------------------------------------------------- layer-adaptive key bits
+# The TurboQuant project article's direction 3: the first four layers get one
+# more key bit (initial_layers_key_bits); later layers keep the base config.
+
+@pytest.mark.parametrize("preset,first_kb", [("turboquant_k3v4_nc", 4), ("turboquant_3bit_nc", 4),
+                                             ("turboquant_4bit_nc", 5)])
+def test_layer_config_first_four_layers_get_one_more_key_bit(preset, first_kb):
+    base = C.from_cache_dtype(preset, 128)
+    for layer in range(8):
+        lc = C.layer_config(base, layer)
+        if layer < 4:
+            assert lc.key_quant_bits == first_kb
+            assert (lc.value_quant_bits, lc.norm_correction, lc.seed, lc.head_dim) == \
+                (base.value_quant_bits, base.norm_correction, base.seed, base.head_dim)
+        else:
+            assert lc == base
+
+
+def test_layer_config_slot_sizes():
+    base = C.from_cache_dtype("turboquant_k3v4_nc", 128)
+    # layers 0-3: 4-bit keys -> the 4bit_nc slot (134 B); from layer 4 the k3v4 slot (118 B)
+    assert [C.layer_config(base, i).slot_size_aligned for i in range(6)] == [134] * 4 + [118] * 2
+    b2 = C.TQConfig(head_dim=128, key_quant_bits=3, value_quant_bits=2, norm_correction=True)
+    assert C.layer_config(b2, 0).slot_size_aligned == 102 and C.layer_config(b2, 4).slot_size_aligned == 86
+
+
+def test_layer_config_fp8_and_explicit_width():
+    k8 = C.from_cache_dtype("turboquant_k8v4", 128)
+    assert C.layer_config(k8, 0) == k8          # no wider form of FP8 keys
+    assert C.layer_config(k8, 0, initial_layers_key_bits=4).key_quant_bits == 4
+    base = C.from_cache_dtype("turboquant_3bit_nc", 128)
+    assert C.layer_config(base, 1, initial_layers_key_bits=8).key_fp8
+    assert C.layer_config(base, 1, initial_layers=0) == base
+    assert C.layer_config(base, 5, initial_layers=6).key_quant_bits == 4
+    with pytest.raises(ValueError):
+        C.layer_config(base, -1)

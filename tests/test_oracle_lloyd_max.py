@@ -18,7 +18,7 @@ def _golden():
         return json.load(f)
 
 
-@pytest.mark.parametrize("levels", [8, 16])
+@pytest.mark.parametrize("levels", [4, 8, 16])
 def test_matches_max_1960_table(levels):
     g = _golden()
     want = np.array(g["levels"][str(levels)]["outputs"])
@@ -36,7 +36,7 @@ def _mse(c):
     return total
 
 
-@pytest.mark.parametrize("levels", [8, 16])
+@pytest.mark.parametrize("levels", [4, 8, 16])
 def test_distortion_matches_max(levels):
     g = _golden()
     want = g["levels"][str(levels)]["mse"]
@@ -55,7 +55,7 @@ def test_centroid_condition(levels):
 
 
 @pytest.mark.parametrize("d", [64, 96, 128])
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_fp32_tables(d, bits):
     c64 = LM.centroids_f64(d, bits)
     assert np.allclose(c64 * math.sqrt(d), LM.standard_normal_table(2 ** bits), rtol=1e-15)
