@@ -240,7 +240,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w = WORKLOADS[args.workload]
-    cfg = tq.config_from_preset(w.preset, w.head_dim) if w.preset else tq.config_init(w.head_dim, w.key_bits, w.value_bits)
+    cfg = tq.config_from_preset(w.preset, w.head_dim) if w.preset else \
+        tq.config_init(w.head_dim, w.key_bits, w.value_bits, w.norm_correction, 42)
     from workloads import sequence_lengths
     pool_bytes = int(sequence_lengths(w).sum()) * w.num_kv_heads * cfg.slot_size_aligned
     n_pools = 1 if pool_bytes > 2 * MALL_BYTES else max(1, -(-3 * MALL_BYTES // max(pool_bytes, 1)))

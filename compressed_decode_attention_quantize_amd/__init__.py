@@ -57,7 +57,7 @@ STATUS_NAMES = {0: "TQ_OK", 1: "TQ_ERR_INVALID_ARG", 2: "TQ_ERR_UNKNOWN_PRESET",
                 3: "TQ_ERR_UNSUPPORTED", 4: "TQ_ERR_WORKSPACE", 5: "TQ_ERR_HIP"}
 F32, BF16, F16 = 0, 1, 2
 
-EXPORTED = ["tq_config_init", "tq_config_from_preset", "tq_slot_size", "tq_page_size",
+EXPORTED = ["tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_slot_size", "tq_page_size",
             "tq_layer_signs", "tq_quantize_append", "tq_decode_workspace_size",
             "tq_decode_attention", "tq_dequant", "tq_last_error", "tq_version"]
 
@@ -96,6 +96,7 @@ _CP = ctypes.POINTER(Config)
 
 _lib.tq_config_init.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _CP]
 _lib.tq_config_from_preset.argtypes = [ctypes.c_char_p, ctypes.c_int, _CP]
+_lib.tq_layer_config.argtypes = [_CP, ctypes.c_int, ctypes.c_int, ctypes.c_int, _CP]
 _lib.tq_slot_size.argtypes = [_CP, ctypes.c_int]
 _lib.tq_slot_size.restype = _i32
 _lib.tq_page_size.argtypes = [_CP, ctypes.c_int, ctypes.c_int]
@@ -110,7 +111,7 @@ _lib.tq_decode_attention.argtypes = [_CP, ctypes.c_int, _P, ctypes.c_int, ctypes
                                      ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _sz,
                                      ctypes.c_int, _P]
 _lib.tq_dequant.argtypes = [_CP, ctypes.c_int, _P, _i64, ctypes.c_int, ctypes.c_int, _P, _i64, _P, _P, _P]
-for _name in ("tq_config_init", "tq_config_from_preset", "tq_layer_signs", "tq_quantize_append",
+for _name in ("tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_layer_signs", "tq_quantize_append",
               "tq_decode_workspace_size", "tq_decode_attention", "tq_dequant"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.tq_last_error.restype = ctypes.c_char_p
@@ -147,6 +148,15 @@ def config_init(head_dim: int, key_bits: int, value_bits: int, norm_correction: 
 def config_from_preset(preset: str, head_dim: int) -> Config:
     c = Config()
     _check(_lib.tq_config_from_preset(preset.encode(), head_dim, ctypes.byref(c)))
+    return c
+
+
+def layer_config(base: Config, layer_idx: int, initial_layers: int = 4,
+                 initial_layers_key_bits: int = 0) -> Config:
+    """Config of one layer under layer-adaptive key bits (0 = base bits + 1)."""
+    c = Config()
+    _check(_lib.tq_layer_config(ctypes.byref(base), layer_idx, initial_layers, initial_layers_key_bits,
+                                ctypes.byref(c)))
     return c
 
 

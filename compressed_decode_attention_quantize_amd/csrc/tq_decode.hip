@@ -239,6 +239,36 @@ struct ValueExpand<3> {
   __device__ static float inv_scale(int c) { return 1.0f / static_cast<float>(1 << pos(c)); }
 };
 
+template <>
+struct ValueExpand<2> {
+  static constexpr int kC0 = 2;
+  // element c sits at bits 2c..2c+1; byte c / 4 holds it, at bit 2 (c % 4)
+  __device__ static constexpr int pos(int c) { return 2 * (c & 3); }
+  __device__ static void run(const uint32_t d[4], half4_t av[8]) {
+    // d[r]: 16 bits (elements 8i..8i+7) of token 4kq + r; byte k of tokens
+    // (0, 1) and (2, 3) into the low and high halves
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t sel = static_cast<uint32_t>(k) | (0x0Cu << 8) | ((4u + k) << 16) | (0x0Cu << 24);
+      const uint32_t x01 = perm(d[1], d[0], sel);
+      const uint32_t x23 = perm(d[3], d[2], sel);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 4 * k + e;
+        const uint32_t m16 = 3u << pos(c);
+        const uint32_t mask = m16 | (m16 << 16);
+        const float off = -(1024.0f + static_cast<float>(1 << pos(c)) * kC0);
+        const uint32_t neg = f16_pair_bits(off, off);
+        u32x2_t v;
+        v[0] = code_pair(x01, mask, neg);
+        v[1] = code_pair(x23, mask, neg);
+        av[c] = __builtin_bit_cast(half4_t, v);
+      }
+    }
+  }
+  __device__ static float inv_scale(int c) { return 1.0f / static_cast<float>(1 << pos(c)); }
+};
+
 // Key operand of one lane: token t = lane % 16, elements kq*D/4 .. +D/4-1 as
 // f16 centroid values (MSE, via the pair table) or FP8-decoded values.
 template <int D, int KB>
@@ -1070,6 +1100,9 @@ int dispatch_decode_group(tq_dtype qd, const DecodeParams &p, hipStream_t s) {
 template <int D>
 int dispatch_decode_bits(const tq_config &c, tq_dtype qd, const DecodeParams &p, hipStream_t s) {
   const int kb = c.key_quant_bits, vb = c.value_quant_bits;
+  if (kb == 3 && vb == 2) return dispatch_decode_group<D, 3, 2>(qd, p, s);
+  if (kb == 4 && vb == 2) return dispatch_decode_group<D, 4, 2>(qd, p, s);
+  if (kb == 8 && vb == 2) return dispatch_decode_group<D, 8, 2>(qd, p, s);
   if (kb == 3 && vb == 3) return dispatch_decode_group<D, 3, 3>(qd, p, s);
   if (kb == 3 && vb == 4) return dispatch_decode_group<D, 3, 4>(qd, p, s);
   if (kb == 4 && vb == 3) return dispatch_decode_group<D, 4, 3>(qd, p, s);

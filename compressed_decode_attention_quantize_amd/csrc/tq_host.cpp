@@ -121,7 +121,7 @@ tq_status check_config(const tq_config *cfg) {
   // are trusted to be the ones tq_config_init wrote).
   if (!cfg) return fail(TQ_ERR_INVALID_ARG, "config is NULL");
   const int d = cfg->head_dim, kb = cfg->key_quant_bits, vb = cfg->value_quant_bits;
-  if (!supported_head_dim(d) || (kb != 3 && kb != 4 && kb != 8) || (vb != 3 && vb != 4))
+  if (!supported_head_dim(d) || (kb != 3 && kb != 4 && kb != 8) || (vb < 2 || vb > 4))
     return fail(TQ_ERR_INVALID_ARG, "config has an unsupported head_dim / bit width");
   const int fp8 = kb == 8;
   const int kp = fp8 ? d : ceil_div_i(d * kb, 8) + 2;
@@ -176,8 +176,8 @@ TQ_EXPORT tq_status tq_config_init(int head_dim, int key_bits, int value_bits, i
     return fail(TQ_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) + " not supported (64, 96, 128)");
   if (key_bits != 3 && key_bits != 4 && key_bits != 8)
     return fail(TQ_ERR_INVALID_ARG, "key_quant_bits must be 3, 4 (MSE) or 8 (FP8), got " + std::to_string(key_bits));
-  if (value_bits != 3 && value_bits != 4)
-    return fail(TQ_ERR_INVALID_ARG, "value_quant_bits must be 3 or 4, got " + std::to_string(value_bits));
+  if (value_bits < 2 || value_bits > 4)
+    return fail(TQ_ERR_INVALID_ARG, "value_quant_bits must be 2, 3 or 4, got " + std::to_string(value_bits));
   tq_config c;
   std::memset(&c, 0, sizeof(c));
   c.head_dim = head_dim;
@@ -223,6 +223,30 @@ TQ_EXPORT tq_status tq_config_from_preset(const char *preset, int head_dim, tq_c
   }
   return fail(TQ_ERR_UNKNOWN_PRESET,
               std::string("Unknown TurboQuant cache dtype: '") + preset + "'. Valid presets: " + valid);
+}
+
+TQ_EXPORT tq_status tq_layer_config(const tq_config *base, int layer_idx, int initial_layers,
+                                    int initial_layers_key_bits, tq_config *out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_layer_config: out is NULL");
+  const tq_status st = check_config(base);
+  if (st != TQ_OK) return st;
+  if (layer_idx < 0 || initial_layers < 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_layer_config: layer_idx and initial_layers must be >= 0");
+  if (initial_layers_key_bits < 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_layer_config: initial_layers_key_bits must be >= 0 (0 = base + 1)");
+  int kb = base->key_quant_bits;
+  if (layer_idx < initial_layers) {
+    if (initial_layers_key_bits > 0)
+      kb = initial_layers_key_bits;
+    else if (!base->key_fp8)
+      kb = base->key_quant_bits + 1;
+  }
+  tq_config c;
+  const tq_status s2 = tq_config_init(base->head_dim, kb, base->value_quant_bits, base->norm_correction,
+                                      base->seed, &c);
+  if (s2 != TQ_OK) return s2;
+  *out = c;
+  return TQ_OK;
 }
 
 TQ_EXPORT int32_t tq_slot_size(const tq_config *cfg, int aligned) {

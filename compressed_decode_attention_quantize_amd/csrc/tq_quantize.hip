@@ -255,6 +255,9 @@ int launch_dequant_t(const DequantParams &p, hipStream_t s) {
 template <int D>
 int dispatch_quantize_bits(const tq_config &c, tq_dtype dt, const QuantParams &p, hipStream_t s) {
   const int kb = c.key_quant_bits, vb = c.value_quant_bits;
+  if (kb == 3 && vb == 2) return launch_quantize_t<D, 3, 2>(dt, p, s);
+  if (kb == 4 && vb == 2) return launch_quantize_t<D, 4, 2>(dt, p, s);
+  if (kb == 8 && vb == 2) return launch_quantize_t<D, 8, 2>(dt, p, s);
   if (kb == 3 && vb == 3) return launch_quantize_t<D, 3, 3>(dt, p, s);
   if (kb == 3 && vb == 4) return launch_quantize_t<D, 3, 4>(dt, p, s);
   if (kb == 4 && vb == 3) return launch_quantize_t<D, 4, 3>(dt, p, s);
@@ -267,6 +270,9 @@ int dispatch_quantize_bits(const tq_config &c, tq_dtype dt, const QuantParams &p
 template <int D>
 int dispatch_dequant_bits(const tq_config &c, const DequantParams &p, hipStream_t s) {
   const int kb = c.key_quant_bits, vb = c.value_quant_bits;
+  if (kb == 3 && vb == 2) return launch_dequant_t<D, 3, 2>(p, s);
+  if (kb == 4 && vb == 2) return launch_dequant_t<D, 4, 2>(p, s);
+  if (kb == 8 && vb == 2) return launch_dequant_t<D, 8, 2>(p, s);
   if (kb == 3 && vb == 3) return launch_dequant_t<D, 3, 3>(p, s);
   if (kb == 3 && vb == 4) return launch_dequant_t<D, 3, 4>(p, s);
   if (kb == 4 && vb == 3) return launch_dequant_t<D, 4, 3>(p, s);

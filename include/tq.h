@@ -15,7 +15,10 @@
  *         ring buffer, whole-chunk compression) and next-directions
  *         section, direction 1 (fused decode attention: single pass over the
  *         compressed data, online softmax block by block, query rotated
- *         forward instead of rotating keys back, no materialised FP16 KV).
+ *         forward instead of rotating keys back, no materialised FP16 KV),
+ *         direction 2 (2-bit values beside 4-bit ones) and direction 3
+ *         (initial_layers_key_bits: the first four layers get one more key
+ *         bit).
  *
  * Conventions for every function:
  *  - Returns a tq_status; never throws or aborts. On failure nothing is
@@ -79,7 +82,7 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 typedef struct {
   int32_t head_dim;          /* 64 | 96 | 128                                 */
   int32_t key_quant_bits;    /* 3 | 4 = Lloyd-Max MSE keys; 8 = FP8 keys      */
-  int32_t value_quant_bits;  /* 3 | 4                                         */
+  int32_t value_quant_bits;  /* 2 | 3 | 4                                     */
   int32_t norm_correction;   /* 0 | 1                                         */
   int64_t seed;              /* base seed (default 42)                        */
   int32_t key_fp8;           /* key_quant_bits == 8                           */
@@ -100,7 +103,9 @@ typedef struct {
 } tq_config;
 
 /* Dataclass constructor ([API] TurboQuantConfig fields). head_dim must be 64,
- * 96 or 128; key_bits 3, 4 or 8; value_bits 3 or 4. Host only. */
+ * 96 or 128; key_bits 3, 4 or 8; value_bits 2, 3 or 4 (2 per [ART]
+ * direction 2; the value field is then ceil(D*2/8) + 4 bytes by the [API]
+ * value_packed_size formula). Host only. */
 tq_status tq_config_init(int head_dim, int key_bits, int value_bits, int norm_correction,
                          int64_t seed, tq_config *out);
 
@@ -111,6 +116,18 @@ tq_status tq_config_init(int head_dim, int key_bits, int value_bits, int norm_co
  * "Unknown TurboQuant cache dtype: '<name>'. Valid presets: turboquant_k8v4,
  * turboquant_4bit_nc, turboquant_k3v4_nc, turboquant_3bit_nc". Host only. */
 tq_status tq_config_from_preset(const char *preset, int head_dim, tq_config *out);
+
+/* Per-layer config for layer-adaptive key bits ([ART] direction 3). For
+ * layer_idx < initial_layers, out = base with key_quant_bits =
+ * initial_layers_key_bits, or base's key bits + 1 when that argument is 0
+ * (an FP8 base then stays FP8: there is no wider FP8 key); for later layers
+ * out = base. All other fields are base's (the layer's seed still comes from
+ * seed + 1337 * layer_idx in the calls that take layer_idx). A width that
+ * tq_config_init rejects (e.g. 5 from a 4-bit base) returns its error;
+ * negative layer_idx or initial_layers returns TQ_ERR_INVALID_ARG. out may
+ * alias base. Host only. */
+tq_status tq_layer_config(const tq_config *base, int layer_idx, int initial_layers,
+                          int initial_layers_key_bits, tq_config *out);
 
 /* Slot bytes per head per position ([API] slot_size / slot_size_aligned):
  * aligned != 0 gives slot_size_aligned. Returns < 0 on a null or invalid

@@ -46,6 +46,54 @@ def test_preset_config_matches_oracle(preset, d):
     assert tq.page_size(c, 8, 16) == 16 * 8 * o.slot_size_aligned
 
 
+@pytest.mark.parametrize("kb,vb", [(3, 2), (4, 2), (8, 2), (3, 3), (8, 3)])
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_custom_bits_config_matches_oracle(d, kb, vb):
+    c = tq.config_init(d, kb, vb, True, 42)
+    o = OC.TQConfig(head_dim=d, key_quant_bits=kb, value_quant_bits=vb, norm_correction=True)
+    for f in ("key_packed_size", "value_packed_size", "slot_size", "slot_size_aligned", "mse_bits",
+              "key_mse_bits", "n_centroids", "wht_block"):
+        assert getattr(c, f) == int(getattr(o, f)), f
+    c32, m32 = OL.tables_f32(d, o.mse_bits)
+    assert np.array_equal(np.array(list(c.centroids), np.float32)[: o.n_centroids].view(np.uint32),
+                          c32.view(np.uint32))
+    assert np.array_equal(np.array(list(c.midpoints), np.float32)[: o.n_centroids - 1].view(np.uint32),
+                          m32.view(np.uint32))
+
+
+@pytest.mark.parametrize("preset", PRESETS + ["k3v2"])
+@pytest.mark.parametrize("layer", [0, 3, 4, 9])
+@pytest.mark.parametrize("initial_bits", [0, 4, 8])
+def test_layer_config_matches_oracle(preset, layer, initial_bits):
+    if preset == "k3v2":
+        base = tq.config_init(128, 3, 2, True, 42)
+        obase = OC.TQConfig(head_dim=128, key_quant_bits=3, value_quant_bits=2, norm_correction=True)
+    else:
+        base = tq.config_from_preset(preset, 128)
+        obase = OC.from_cache_dtype(preset, 128)
+    want = OC.layer_config(obase, layer, initial_layers_key_bits=initial_bits or None)
+    if want.key_quant_bits not in (3, 4, 8):   # e.g. 5 bits from a 4-bit base: not built
+        with pytest.raises(tq.TQError) as ei:
+            tq.layer_config(base, layer, 4, initial_bits)
+        assert ei.value.status == 1
+        return
+    c = tq.layer_config(base, layer, 4, initial_bits)
+    for f in ("head_dim", "key_quant_bits", "value_quant_bits", "seed", "slot_size_aligned", "n_centroids"):
+        assert getattr(c, f) == int(getattr(want, f)), f
+    assert bool(c.norm_correction) == want.norm_correction
+    assert np.array_equal(np.array(list(c.centroids), np.float32)[: want.n_centroids],
+                          OL.tables_f32(128, want.mse_bits)[0])
+
+
+def test_layer_config_argument_errors():
+    base = tq.config_from_preset("turboquant_k3v4_nc", 128)
+    for args in ((-1, 4, 0), (0, -1, 0), (0, 4, -2)):
+        with pytest.raises(tq.TQError) as ei:
+            tq.layer_config(base, *args)
+        assert ei.value.status == 1
+    assert tq.layer_config(base, 0, 0, 0).key_quant_bits == 3   # no initial layers
+
+
 @pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("bits", [3, 4])
 def test_tables_bit_equal_to_oracle(d, bits):
@@ -71,7 +119,8 @@ def test_unknown_preset_error_text():
                                 "turboquant_k8v4, turboquant_4bit_nc, turboquant_k3v4_nc, turboquant_3bit_nc")
 
 
-@pytest.mark.parametrize("args,status", [((100, 3, 4), 3), ((128, 5, 4), 1), ((128, 3, 2), 1), ((256, 3, 4), 3)])
+@pytest.mark.parametrize("args,status", [((100, 3, 4), 3), ((128, 5, 4), 1), ((128, 3, 1), 1), ((128, 3, 5), 1),
+                                         ((256, 3, 4), 3)])
 def test_config_init_rejects(args, status):
     with pytest.raises(tq.TQError) as ei:
         tq.config_init(*args)

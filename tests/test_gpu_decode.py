@@ -86,6 +86,11 @@ SCEN = {
     # ring capacity not a multiple of the 64-token ring chunk; a full chunk,
     # a partial second chunk and a ring-only sequence
     "d96_k3v4_ring100": (96, 3, 4, True, 16, 4, [50, 300, 0], [100, 70, 64], 100),
+    # 2-bit values at each column packing (G = 4, 8, 16 query heads per KV head)
+    "k3v2_nc": (128, 3, 2, True, 32, 8, [1500, 31, 0], None, 0),
+    "k4v2_g8_ring": (128, 4, 2, True, 16, 2, [600, 17], [40, 128], 128),
+    "d96_k8v2": (96, 8, 2, False, 12, 4, [257, 64], None, 0),
+    "d64_k3v2_g16": (64, 3, 2, True, 32, 2, [400], None, 0),
 }
 
 
@@ -155,6 +160,38 @@ def test_layer_and_scale():
     cfg, ocfg, pool_np, tables, q, ring = _scenario(128, 4, 4, True, 8, 2, lens, seed=21, layer=6)
     got, want = _run(cfg, ocfg, pool_np, tables, lens, q, ring, layer=6, scale=0.05)
     assert per_head_rel_l2(got, want) <= ATTN_RTOL
+
+
+def test_layer_adaptive_key_bits():
+    """Layer-adaptive key bits end to end: each layer's config from
+    tq.layer_config (4-bit keys below layer 4, the base 3-bit keys from layer
+    4), quantize-append on the GPU with that layer's signs, slot bytes equal to
+    the oracle's layer_config encoding, decode within tolerance."""
+    from oracle import config as OC
+    base = tq.config_from_preset("turboquant_k3v4_nc", 128)
+    obase = oracle_cfg(base)
+    n, hkv, hq, bs = 300, 2, 8, 16
+    rng = np.random.default_rng(33)
+    k = torch.from_numpy(rng.standard_normal((n, hkv, 128)).astype(np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((n, hkv, 128)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((1, hq, 128)).astype(np.float32)).to(torch.bfloat16)
+    nblk = math.ceil(n / bs)
+    tables = rng.permutation(nblk).astype(np.int32)[None]
+    pos = np.arange(n)
+    mapping = tables[0, pos // bs].astype(np.int64) * bs + pos % bs
+    for layer, want_kb in ((2, 4), (4, 3)):
+        announce(f"decode layer-adaptive layer={layer}")
+        cfg = tq.layer_config(base, layer)
+        ocfg = OC.layer_config(obase, layer)
+        assert cfg.key_quant_bits == ocfg.key_quant_bits == want_kb
+        pool = torch.zeros((nblk, hkv, bs, cfg.slot_size_aligned), dtype=torch.uint8, device="cuda")
+        tq.quantize_append(cfg, layer, k.cuda(), v.cuda(), torch.from_numpy(mapping).cuda(), pool)
+        pool_np = oracle_pool(ocfg, layer, k.float().numpy(), v.float().numpy(), mapping, nblk, hkv, bs)
+        assert np.array_equal(pool.cpu().numpy(), pool_np)
+        out = tq.decode_attention(cfg, layer, q.cuda(), pool, torch.from_numpy(tables).cuda(),
+                                  torch.tensor([n], dtype=torch.int32).cuda(), n)
+        want = OA.decode_attention(q.float().numpy(), pool_np, tables, [n], ocfg, layer)
+        assert per_head_rel_l2(out.cpu().numpy(), want) <= ATTN_RTOL
 
 
 def test_split_invariance_and_determinism():

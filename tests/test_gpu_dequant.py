@@ -14,7 +14,8 @@ tq = pytest.importorskip("compressed_decode_attention_quantize_amd")
 
 @pytest.mark.parametrize("d,kb,vb,nc", [(64, 3, 4, False), (96, 3, 4, True), (128, 8, 4, False),
                                         (128, 4, 4, True), (128, 3, 3, True), (128, 4, 3, False),
-                                        (96, 4, 3, True)])
+                                        (96, 4, 3, True), (128, 3, 2, True), (96, 8, 2, False),
+                                        (64, 4, 2, True)])
 def test_dequant_bit_exact(d, kb, vb, nc):
     announce(f"dequant d={d} kb={kb} vb={vb} nc={nc}")
     cfg = tq.config_init(d, kb, vb, nc, 42)

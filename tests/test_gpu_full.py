@@ -32,7 +32,7 @@ def _picks(w):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["tiny", "k8v4", "4bit_nc", "3bit_nc", "k3v4_nc"])
+@pytest.mark.parametrize("name", ["tiny", "k8v4", "4bit_nc", "3bit_nc", "k3v4_nc", "k3v2_nc"])
 def test_full_size_sampled_sequences(name):
     w = WORKLOADS[name]
     picks = _picks(w)

@@ -39,6 +39,8 @@ CASES = [
     (64, 3, 4, False), (64, 4, 3, False), (64, 8, 4, False),
     (96, 3, 4, True), (96, 4, 4, False), (96, 8, 3, False),
     (128, 8, 4, False), (128, 4, 4, True), (128, 3, 3, True), (128, 3, 4, True), (128, 4, 3, False),
+    # 2-bit values
+    (64, 8, 2, False), (96, 3, 2, True), (128, 3, 2, True), (128, 4, 2, False),
 ]
 
 
