@@ -87,8 +87,8 @@ struct Geo {
   // a tile buffer: the tile plus slack for the funnel-shifted reads that run
   // up to 7 bytes past a field, rounded to 16 bytes
   static constexpr int kTileBuf = ((kTileBytes + 16) + 15) / 16 * 16;
-  // one wave's LDS: two tile buffers (double buffering), or the queries
-  static constexpr int kScratch = (2 * kTileBuf > kQBytes ? 2 * kTileBuf : kQBytes);
+  // one wave's LDS: `bufs` tile buffers, or the queries
+  static constexpr int scratch_bytes(int bufs) { return bufs * kTileBuf > kQBytes ? bufs * kTileBuf : kQBytes; }
   static constexpr int kLut = KB == 4 ? 256 : (KB == 3 ? 64 : 1);
   static_assert(kSlot % 2 == 0, "slot size must be even");
 };
@@ -121,6 +121,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// Wait until this wave's LDS reads have returned (s_waitcnt lgkmcnt(0)).
+// A direct HBM -> LDS load writes LDS through the memory path, unordered with
+// the wave's earlier ds_read instructions; without this wait a load into a
+// buffer can land before earlier reads of that buffer have executed.
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int N>
 struct Words {
@@ -356,9 +362,15 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int S = GE::kSlot;
   constexpr int KM = GE::kKM;
   constexpr int GP = 16 / NB;
+  // Tile buffers per wave. MSE keys with NB > 1 keep all NB tiles of a macro
+  // tile in LDS until the value phase re-reads their codes there (NB + 1
+  // buffers: the next tile loads into the spare one); otherwise two buffers,
+  // the value code words held in registers across the softmax.
+  constexpr bool kValLds = GE::kMse && NB > 1;
+  constexpr int kBufs = kValLds ? NB + 1 : 2;
 
   __shared__ uint32_t lut[GE::kLut];
-  __shared__ __align__(16) uint32_t scratch[kWaves][GE::kScratch / 4];
+  __shared__ __align__(16) uint32_t scratch[kWaves][GE::scratch_bytes(kBufs) / 4];
   // per-token scalars of the macro tile: norm * scale (< 0: masked), s', z' + c0 s', ||c||^2
   __shared__ __align__(16) float tokf[kWaves][4][NB][16];
 
@@ -583,21 +595,24 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     const uint8_t *src = p.pool + ((static_cast<int64_t>(ok_next ? phys : 0) * p.num_kv_heads + h) * p.block_size + off) *
                                       static_cast<int64_t>(S);
     const uint32_t dst = lds_offset(scratch[wave]) + bsel * GE::kTileBuf;
+    wait_lds_reads();  // earlier reads of this buffer (or the query plane) have executed
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int c = lane + 64 * k;
       if (c < GE::kTileChunks) load_lds_16(src + 16 * c, dst + 1024 * k);
     }
   };
-  wave_lds_sync();  // the query plane reads are done before tile loads overwrite it
-  issue(begin, 0);
+  issue(begin, 0);  // waits for the query plane reads before overwriting it
 
   const float c0 = static_cast<float>(VX::kC0);
   const float inv_sigma = 1.0f / p.centroid_scale;
   const bool nc = GE::kMse && p.norm_correction;
   int bsel = 0;
+  // LDS byte offset of element group col's value codes in token 4kq's slot
+  const uint32_t val_off = static_cast<uint32_t>(4 * kq * S + GE::kKeyBytes + VB * col);
   for (int mt0 = begin; mt0 < end; mt0 += NB * kTile) {
-    uint32_t vraw[NB][4];
+    uint32_t vraw[kValLds ? 1 : NB][4];
+    int tbuf[NB];  // buffer of tile i (wave-uniform)
     float4_t sraw = {0.0f, 0.0f, 0.0f, 0.0f};
     // ---- phase A, per tile: scores into the tile's column group, value
     // code words kept in registers, per-token scalars to LDS
@@ -607,14 +622,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       if (tile0 < end) {
         const int ntok = min(kTile, end - tile0);
         const bool tile_ok = ok_next;
+        const int nsel = bsel + 1 == kBufs ? 0 : bsel + 1;
         if (tile0 + kTile < end) {
-          issue(tile0 + kTile, bsel ^ 1);
+          issue(tile0 + kTile, nsel);
           wait_vmcnt<kLoads>();  // this tile's loads are done, the next tile's may run
         } else {
           wait_vmcnt<0>();
         }
         const uint32_t *tw = scr + bsel * (GE::kTileBuf / 4);  // this tile's bytes as words
-        bsel ^= 1;
+        tbuf[i] = bsel;
+        bsel = nsel;
 
         // per-token scalars: lane t < 16 reads its slot's norm / scale / zero
         if (lane < 16) {
@@ -654,19 +671,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         }
 
         // value codes of element group col for tokens 4kq..4kq+3
-        if (col < GE::kGroups) {
+        if constexpr (!kValLds) {
+          if (col < GE::kGroups) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            vraw[i][r] = lds_bytes<VB>(tw, static_cast<uint32_t>((4 * kq + r) * S + GE::kKeyBytes + VB * col)).w[0];
-        } else {
+            for (int r = 0; r < 4; ++r) vraw[i][r] = lds_bytes<VB>(tw, val_off + r * S).w[0];
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) vraw[i][r] = 0u;
+            for (int r = 0; r < 4; ++r) vraw[i][r] = 0u;
+          }
         }
       } else {
         // tile slot past the end of the segment: all its tokens masked
         if (lane < 16) tokf[wave][0][i][lane] = -1.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vraw[i][r] = 0u;
+        tbuf[i] = 0;
       }
     }
 
@@ -732,7 +749,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         const half4_t pvh = __builtin_bit_cast(half4_t, bh);
         const half4_t pvl = __builtin_bit_cast(half4_t, bl);
         half4_t av[8];
-        VX::run(vraw[i], av);  // rows col >= kGroups are padding and never written out
+        if constexpr (kValLds) {
+          // the tile is still in its buffer: the next load went to the spare one
+          const uint32_t *tw = scr + tbuf[i] * (GE::kTileBuf / 4);
+          uint32_t vr[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? lds_bytes<VB>(tw, val_off + r * S).w[0] : 0u;
+          VX::run(vr, av);  // rows col >= kGroups are padding and never written out
+        } else {
+          VX::run(vraw[i], av);
+        }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[c], pvh, acc[c], 0, 0, 0);

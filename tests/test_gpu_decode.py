@@ -214,6 +214,29 @@ def test_split_invariance_and_determinism():
     assert np.array_equal(again.view(np.uint32), outs[1].view(np.uint32))
 
 
+def test_workspace_contents_do_not_matter():
+    """The result depends on the inputs only: a workspace holding NaN or
+    finite garbage from earlier use gives the same outputs (every partial the
+    merge reads is written in the same call), at one-tile and default split
+    sizes, over repeated calls."""
+    announce("decode garbage workspace")
+    lens = [1777, 900, 3]
+    cfg, ocfg, pool_np, tables, q, ring = _scenario(128, 4, 4, True, 16, 4, lens, [40, 128, 0], 128, seed=4)
+    pool = torch.from_numpy(pool_np).cuda()
+    kw = dict(ring_k=ring[0].cuda(), ring_v=ring[1].cuda(), ring_lens=torch.from_numpy(ring[2]).cuda())
+    qd, td, ld = q.cuda(), torch.from_numpy(tables).cuda(), torch.tensor(lens, dtype=torch.int32).cuda()
+    want = OA.decode_attention(q.float().numpy(), pool_np, tables, lens, ocfg, 0, ring_k=ring[0].float().numpy(),
+                               ring_v=ring[1].float().numpy(), ring_lens=ring[2])
+    for split in (16, 0):
+        need, _ = tq.decode_workspace_size(cfg, len(lens), 16, max(lens), 128, split)
+        for fill in (0xff, 0x41, 0x7f) * 2:
+            ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+            out = tq.decode_attention(cfg, 0, qd, pool, td, ld, max(lens), workspace=ws, split_tokens=split, **kw)
+            err = per_head_rel_l2(out.cpu().numpy(), want)
+            announce(f"  split={split} fill={fill:#x}: rel L2 {err:.2e}")
+            assert err <= ATTN_RTOL
+
+
 def test_empty_context_gives_zeros():
     announce("decode empty")
     cfg = tq.config_from_preset("turboquant_3bit_nc", 128)
