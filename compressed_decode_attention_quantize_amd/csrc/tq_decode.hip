@@ -182,29 +182,36 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t x, uint32_t mask, uint32_
 // Value codes of element group i (8 elements) for tokens 4kq..4kq+3 as the
 // A operands of the eight value MFMAs (element 8i+c in MFMA c), with the
 // per-element power-of-two scales the expansion leaves (inv_scale[c]).
+// prep() gathers the tokens' code bytes into 16-bit halves (token pairs
+// (0, 1) and (2, 3) in the two words of each selection); get(c) expands
+// element c from them.
 template <int VB>
 struct ValueExpand;
 
 template <>
 struct ValueExpand<4> {
   static constexpr int kC0 = 8;
-  __device__ static void run(const uint32_t d[4], half4_t av[8]) {
+  struct Prep {
+    uint32_t x[4][2];  // byte k of tokens (0, 1) and (2, 3): elements 2k, 2k + 1
+  };
+  __device__ static void prep(const uint32_t d[4], Prep &pr) {
     // d[r]: 8 nibbles (elements 8i..8i+7) of token 4kq + r
-    const uint32_t off_even = f16_pair_bits(-(1024.0f + kC0), -(1024.0f + kC0));
-    const uint32_t off_odd = f16_pair_bits(-(1024.0f + 16.0f * kC0), -(1024.0f + 16.0f * kC0));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t sel = static_cast<uint32_t>(k) | (0x0Cu << 8) | ((4u + k) << 16) | (0x0Cu << 24);
-      const uint32_t x01 = perm(d[1], d[0], sel);
-      const uint32_t x23 = perm(d[3], d[2], sel);
-      u32x2_t e, o;
-      e[0] = code_pair(x01, 0x000F000Fu, off_even);
-      e[1] = code_pair(x23, 0x000F000Fu, off_even);
-      o[0] = code_pair(x01, 0x00F000F0u, off_odd);
-      o[1] = code_pair(x23, 0x00F000F0u, off_odd);
-      av[2 * k] = __builtin_bit_cast(half4_t, e);
-      av[2 * k + 1] = __builtin_bit_cast(half4_t, o);
+      pr.x[k][0] = perm(d[1], d[0], sel);
+      pr.x[k][1] = perm(d[3], d[2], sel);
     }
+  }
+  __device__ static half4_t get(const Prep &pr, int c) {
+    const bool odd = c & 1;
+    const float off = -(1024.0f + (odd ? 16.0f : 1.0f) * kC0);
+    const uint32_t neg = f16_pair_bits(off, off);
+    const uint32_t mask = odd ? 0x00F000F0u : 0x000F000Fu;
+    u32x2_t v;
+    v[0] = code_pair(pr.x[c >> 1][0], mask, neg);
+    v[1] = code_pair(pr.x[c >> 1][1], mask, neg);
+    return __builtin_bit_cast(half4_t, v);
   }
   __device__ static float inv_scale(int c) { return (c & 1) ? (1.0f / 16.0f) : 1.0f; }
 };
@@ -213,34 +220,35 @@ template <>
 struct ValueExpand<3> {
   static constexpr int kC0 = 4;
   // element c sits at bits 3c..3c+2; after the byte selection below its
-  // field starts at bit kPos[c] of a 16-bit half.
+  // field starts at bit pos(c) of a 16-bit half.
   __device__ static constexpr int pos(int c) {
     return c == 0 ? 0 : c == 1 ? 3 : c == 2 ? 6 : c == 3 ? 1 : c == 4 ? 4 : c == 5 ? 7 : c == 6 ? 2 : 5;
   }
-  __device__ static void run(const uint32_t d[4], half4_t av[8]) {
+  struct Prep {
+    uint32_t x[3][2];  // bits 0..15, 8..23 and 16..23 of tokens (0, 1) and (2, 3)
+  };
+  __device__ static void prep(const uint32_t d[4], Prep &pr) {
     // d[r]: 24 bits (elements 8i..8i+7) of token 4kq + r
     constexpr uint32_t selX = 0u | (1u << 8) | (4u << 16) | (5u << 24);     // bits 0..15
     constexpr uint32_t selY = 1u | (2u << 8) | (5u << 16) | (6u << 24);     // bits 8..23
     constexpr uint32_t selZ = 2u | (0x0Cu << 8) | (6u << 16) | (0x0Cu << 24);  // bits 16..23
-    uint32_t xs[3][2];
-    xs[0][0] = perm(d[1], d[0], selX);
-    xs[0][1] = perm(d[3], d[2], selX);
-    xs[1][0] = perm(d[1], d[0], selY);
-    xs[1][1] = perm(d[3], d[2], selY);
-    xs[2][0] = perm(d[1], d[0], selZ);
-    xs[2][1] = perm(d[3], d[2], selZ);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int src = c < 3 ? 0 : (c < 6 ? 1 : 2);
-      const uint32_t m16 = 7u << pos(c);
-      const uint32_t mask = m16 | (m16 << 16);
-      const float off = -(1024.0f + static_cast<float>(1 << pos(c)) * kC0);
-      const uint32_t neg = f16_pair_bits(off, off);
-      u32x2_t v;
-      v[0] = code_pair(xs[src][0], mask, neg);
-      v[1] = code_pair(xs[src][1], mask, neg);
-      av[c] = __builtin_bit_cast(half4_t, v);
-    }
+    pr.x[0][0] = perm(d[1], d[0], selX);
+    pr.x[0][1] = perm(d[3], d[2], selX);
+    pr.x[1][0] = perm(d[1], d[0], selY);
+    pr.x[1][1] = perm(d[3], d[2], selY);
+    pr.x[2][0] = perm(d[1], d[0], selZ);
+    pr.x[2][1] = perm(d[3], d[2], selZ);
+  }
+  __device__ static half4_t get(const Prep &pr, int c) {
+    const int src = c < 3 ? 0 : (c < 6 ? 1 : 2);
+    const uint32_t m16 = 7u << pos(c);
+    const uint32_t mask = m16 | (m16 << 16);
+    const float off = -(1024.0f + static_cast<float>(1 << pos(c)) * kC0);
+    const uint32_t neg = f16_pair_bits(off, off);
+    u32x2_t v;
+    v[0] = code_pair(pr.x[src][0], mask, neg);
+    v[1] = code_pair(pr.x[src][1], mask, neg);
+    return __builtin_bit_cast(half4_t, v);
   }
   __device__ static float inv_scale(int c) { return 1.0f / static_cast<float>(1 << pos(c)); }
 };
@@ -250,27 +258,27 @@ struct ValueExpand<2> {
   static constexpr int kC0 = 2;
   // element c sits at bits 2c..2c+1; byte c / 4 holds it, at bit 2 (c % 4)
   __device__ static constexpr int pos(int c) { return 2 * (c & 3); }
-  __device__ static void run(const uint32_t d[4], half4_t av[8]) {
-    // d[r]: 16 bits (elements 8i..8i+7) of token 4kq + r; byte k of tokens
-    // (0, 1) and (2, 3) into the low and high halves
+  struct Prep {
+    uint32_t x[2][2];  // byte k of tokens (0, 1) and (2, 3): elements 4k..4k+3
+  };
+  __device__ static void prep(const uint32_t d[4], Prep &pr) {
+    // d[r]: 16 bits (elements 8i..8i+7) of token 4kq + r
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const uint32_t sel = static_cast<uint32_t>(k) | (0x0Cu << 8) | ((4u + k) << 16) | (0x0Cu << 24);
-      const uint32_t x01 = perm(d[1], d[0], sel);
-      const uint32_t x23 = perm(d[3], d[2], sel);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = 4 * k + e;
-        const uint32_t m16 = 3u << pos(c);
-        const uint32_t mask = m16 | (m16 << 16);
-        const float off = -(1024.0f + static_cast<float>(1 << pos(c)) * kC0);
-        const uint32_t neg = f16_pair_bits(off, off);
-        u32x2_t v;
-        v[0] = code_pair(x01, mask, neg);
-        v[1] = code_pair(x23, mask, neg);
-        av[c] = __builtin_bit_cast(half4_t, v);
-      }
+      pr.x[k][0] = perm(d[1], d[0], sel);
+      pr.x[k][1] = perm(d[3], d[2], sel);
     }
+  }
+  __device__ static half4_t get(const Prep &pr, int c) {
+    const uint32_t m16 = 3u << pos(c);
+    const uint32_t mask = m16 | (m16 << 16);
+    const float off = -(1024.0f + static_cast<float>(1 << pos(c)) * kC0);
+    const uint32_t neg = f16_pair_bits(off, off);
+    u32x2_t v;
+    v[0] = code_pair(pr.x[c >> 2][0], mask, neg);
+    v[1] = code_pair(pr.x[c >> 2][1], mask, neg);
+    return __builtin_bit_cast(half4_t, v);
   }
   __device__ static float inv_scale(int c) { return 1.0f / static_cast<float>(1 << pos(c)); }
 };
@@ -737,32 +745,73 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
 
     // ---- phase C, per tile: value MFMAs with the weights of the tile's
     // column group only (zero elsewhere)
+    // value code bytes of tile i for this lane's element group, gathered
+    auto prep_tile = [&](int i, typename VX::Prep &pr) {
+      if constexpr (kValLds) {
+        // the tile is still in its buffer: the next load went to the spare one
+        const uint32_t *tw = scr + tbuf[i] * (GE::kTileBuf / 4);
+        uint32_t vr[4];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (mt0 + i * kTile < end) {
-        const bool mine = my_tile == i;
-        u32x2_t bh, bl;
-        bh[0] = mine ? hw[0] : 0u;
-        bh[1] = mine ? hw[1] : 0u;
-        bl[0] = mine ? lw[0] : 0u;
-        bl[1] = mine ? lw[1] : 0u;
-        const half4_t pvh = __builtin_bit_cast(half4_t, bh);
-        const half4_t pvl = __builtin_bit_cast(half4_t, bl);
-        half4_t av[8];
-        if constexpr (kValLds) {
-          // the tile is still in its buffer: the next load went to the spare one
-          const uint32_t *tw = scr + tbuf[i] * (GE::kTileBuf / 4);
-          uint32_t vr[4];
+        for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? lds_bytes<VB>(tw, val_off + r * S).w[0] : 0u;
+        VX::prep(vr, pr);  // rows col >= kGroups are padding and never written out
+      } else {
+        VX::prep(vraw[i], pr);
+      }
+    };
+    if constexpr (NB >= 2) {
+      // Tiles in pairs: one 16x16x32 MFMA takes tokens 4kq..4kq+3 of tile i
+      // in K slots 8kq..8kq+3 and those of tile i+1 in 8kq+4..8kq+7, with
+      // each tile's weights masked to its own column group.
 #pragma unroll
-          for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? lds_bytes<VB>(tw, val_off + r * S).w[0] : 0u;
-          VX::run(vr, av);  // rows col >= kGroups are padding and never written out
-        } else {
-          VX::run(vraw[i], av);
+      for (int i = 0; i < NB; i += 2) {
+        if (mt0 + i * kTile < end) {
+          const bool has1 = mt0 + (i + 1) * kTile < end;
+          const bool m0 = my_tile == i, m1 = my_tile == i + 1;
+          u32x4_t bh, bl;
+          bh[0] = m0 ? hw[0] : 0u;
+          bh[1] = m0 ? hw[1] : 0u;
+          bh[2] = m1 ? hw[0] : 0u;
+          bh[3] = m1 ? hw[1] : 0u;
+          bl[0] = m0 ? lw[0] : 0u;
+          bl[1] = m0 ? lw[1] : 0u;
+          bl[2] = m1 ? lw[0] : 0u;
+          bl[3] = m1 ? lw[1] : 0u;
+          const half8_t pvh = __builtin_bit_cast(half8_t, bh);
+          const half8_t pvl = __builtin_bit_cast(half8_t, bl);
+          typename VX::Prep p0, p1;
+          prep_tile(i, p0);
+          // past the end of the range the second half's weights are zero
+          // (masked tokens), so any finite codes do: reuse the first tile's
+          if (has1) prep_tile(i + 1, p1);
+          else p1 = p0;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const half8_t av = __builtin_shufflevector(VX::get(p0, c), VX::get(p1, c), 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pvh, acc[c], 0, 0, 0);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pvl, acc[c], 0, 0, 0);
+          }
         }
+      }
+    } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[c], pvh, acc[c], 0, 0, 0);
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[c], pvl, acc[c], 0, 0, 0);
+      for (int i = 0; i < NB; ++i) {
+        if (mt0 + i * kTile < end) {
+          const bool mine = my_tile == i;
+          u32x2_t bh, bl;
+          bh[0] = mine ? hw[0] : 0u;
+          bh[1] = mine ? hw[1] : 0u;
+          bl[0] = mine ? lw[0] : 0u;
+          bl[1] = mine ? lw[1] : 0u;
+          const half4_t pvh = __builtin_bit_cast(half4_t, bh);
+          const half4_t pvl = __builtin_bit_cast(half4_t, bl);
+          typename VX::Prep p0;
+          prep_tile(i, p0);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const half4_t av = VX::get(p0, c);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pvh, acc[c], 0, 0, 0);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pvl, acc[c], 0, 0, 0);
+          }
         }
       }
     }
