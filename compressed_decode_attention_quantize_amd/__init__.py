@@ -57,8 +57,9 @@ STATUS_NAMES = {0: "TQ_OK", 1: "TQ_ERR_INVALID_ARG", 2: "TQ_ERR_UNKNOWN_PRESET",
                 3: "TQ_ERR_UNSUPPORTED", 4: "TQ_ERR_WORKSPACE", 5: "TQ_ERR_HIP"}
 F32, BF16, F16 = 0, 1, 2
 
-EXPORTED = ["tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_slot_size", "tq_page_size",
-            "tq_layer_signs", "tq_quantize_append", "tq_decode_workspace_size",
+EXPORTED = ["tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_boundary_skip_layers",
+            "tq_attn_page_size_1_token", "tq_slot_size", "tq_page_size",
+            "tq_layer_signs", "tq_quantize_append", "tq_ring_flush", "tq_ring_append", "tq_decode_workspace_size",
             "tq_decode_attention", "tq_dequant", "tq_last_error", "tq_version"]
 
 
@@ -97,6 +98,14 @@ _CP = ctypes.POINTER(Config)
 _lib.tq_config_init.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _CP]
 _lib.tq_config_from_preset.argtypes = [ctypes.c_char_p, ctypes.c_int, _CP]
 _lib.tq_layer_config.argtypes = [_CP, ctypes.c_int, ctypes.c_int, ctypes.c_int, _CP]
+_lib.tq_boundary_skip_layers.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.c_int]
+_lib.tq_boundary_skip_layers.restype = ctypes.c_int
+_lib.tq_attn_page_size_1_token.argtypes = [_CP, ctypes.c_int, ctypes.c_int]
+_lib.tq_attn_page_size_1_token.restype = _i64
+_lib.tq_ring_flush.argtypes = [_CP, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, _P, _i64, ctypes.c_int, _P]
+_lib.tq_ring_append.argtypes = [_CP, _P, _P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P]
 _lib.tq_slot_size.argtypes = [_CP, ctypes.c_int]
 _lib.tq_slot_size.restype = _i32
 _lib.tq_page_size.argtypes = [_CP, ctypes.c_int, ctypes.c_int]
@@ -112,6 +121,7 @@ _lib.tq_decode_attention.argtypes = [_CP, ctypes.c_int, _P, ctypes.c_int, ctypes
                                      ctypes.c_int, _P]
 _lib.tq_dequant.argtypes = [_CP, ctypes.c_int, _P, _i64, ctypes.c_int, ctypes.c_int, _P, _i64, _P, _P, _P]
 for _name in ("tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_layer_signs", "tq_quantize_append",
+              "tq_ring_flush", "tq_ring_append",
               "tq_decode_workspace_size", "tq_decode_attention", "tq_dequant"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.tq_last_error.restype = ctypes.c_char_p
@@ -158,6 +168,23 @@ def layer_config(base: Config, layer_idx: int, initial_layers: int = 4,
     _check(_lib.tq_layer_config(ctypes.byref(base), layer_idx, initial_layers, initial_layers_key_bits,
                                 ctypes.byref(c)))
     return c
+
+
+def boundary_skip_layers(num_layers: int, n: int = 2, hybrid: bool = False) -> list:
+    """Layer indices (as strings) that keep the unquantized cache."""
+    cnt = _lib.tq_boundary_skip_layers(num_layers, n, int(bool(hybrid)), None, 0)
+    if cnt < 0:
+        raise TQError(1, last_error())
+    buf = (ctypes.c_int32 * max(cnt, 1))()
+    _lib.tq_boundary_skip_layers(num_layers, n, int(bool(hybrid)), buf, cnt)
+    return [str(buf[i]) for i in range(cnt)]
+
+
+def attn_page_size_1_token(cfg: Config, num_kv_heads: int, skip_dtype_bytes: int = 0) -> int:
+    n = _lib.tq_attn_page_size_1_token(ctypes.byref(cfg), num_kv_heads, skip_dtype_bytes)
+    if n < 0:
+        raise TQError(1, last_error())
+    return n
 
 
 def slot_size(cfg: Config, aligned: bool = True) -> int:
@@ -240,6 +267,58 @@ def quantize_append(cfg: Config, layer_idx: int, k, v, slot_mapping, kv_pool, st
                                    v.stride(0) if t_count > 1 else hkv * cfg.head_dim,
                                    slot_mapping.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
                                    kv_pool.shape[2], s))
+
+
+def ring_flush(cfg: Config, layer_idx: int, ring_k, ring_v, ring_lens, seq_lens, block_tables, kv_pool,
+               stream=None) -> None:
+    """Compress every full ring (bf16 [B, Hkv, cap, D]) into the pool at its
+    sequence's next positions; updates ring_lens / seq_lens (int32 [B]) in place."""
+    torch = _torch()
+    _dev(ring_k, "ring_k", torch.bfloat16)
+    _dev(ring_v, "ring_v", torch.bfloat16)
+    _dev(ring_lens, "ring_lens", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(kv_pool, "kv_pool", torch.uint8)
+    if ring_k.dim() != 4 or ring_k.shape != ring_v.shape or ring_k.shape[3] != cfg.head_dim \
+            or not ring_k.is_contiguous() or not ring_v.is_contiguous():
+        raise ValueError(f"ring_k/ring_v must be contiguous bf16 [B, Hkv, cap, {cfg.head_dim}]")
+    bsz, hkv, cap, _ = ring_k.shape
+    if ring_lens.shape != (bsz,) or seq_lens.shape != (bsz,) or block_tables.dim() != 2 \
+            or block_tables.shape[0] != bsz or not block_tables.is_contiguous():
+        raise ValueError("ring_lens/seq_lens must be [B] and block_tables contiguous [B, max_blocks]")
+    if kv_pool.dim() != 4 or kv_pool.shape[1] != hkv or kv_pool.shape[3] != cfg.slot_size_aligned \
+            or not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be contiguous [num_blocks, Hkv, block_size, slot_size_aligned]")
+    s = stream if stream is not None else _stream_ptr(ring_k)
+    _check(_lib.tq_ring_flush(ctypes.byref(cfg), layer_idx, ring_k.data_ptr(), ring_v.data_ptr(), cap,
+                              ring_lens.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr(),
+                              block_tables.shape[1], bsz, hkv, kv_pool.data_ptr(), kv_pool.shape[0],
+                              kv_pool.shape[2], s))
+
+
+def ring_append(cfg: Config, k_new, v_new, ring_k, ring_v, ring_lens, stream=None) -> None:
+    """Copy each sequence's new token (bf16 [B, Hkv, D]) to the end of its ring."""
+    torch = _torch()
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (ring_k, "ring_k"), (ring_v, "ring_v")):
+        _dev(t, n, torch.bfloat16)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    _dev(ring_lens, "ring_lens", torch.int32)
+    bsz, hkv, cap, d = ring_k.shape
+    if k_new.shape != (bsz, hkv, d) or v_new.shape != k_new.shape or ring_v.shape != ring_k.shape \
+            or d != cfg.head_dim or ring_lens.shape != (bsz,):
+        raise ValueError("k_new/v_new must be [B, Hkv, D] matching the ring [B, Hkv, cap, D]")
+    s = stream if stream is not None else _stream_ptr(ring_k)
+    _check(_lib.tq_ring_append(ctypes.byref(cfg), k_new.data_ptr(), v_new.data_ptr(), bsz, hkv, ring_k.data_ptr(),
+                               ring_v.data_ptr(), cap, ring_lens.data_ptr(), s))
+
+
+def ring_step(cfg: Config, layer_idx: int, k_new, v_new, ring_k, ring_v, ring_lens, seq_lens, block_tables,
+              kv_pool, stream=None) -> None:
+    """One decode step's write: flush full rings as whole chunks, then append."""
+    ring_flush(cfg, layer_idx, ring_k, ring_v, ring_lens, seq_lens, block_tables, kv_pool, stream)
+    ring_append(cfg, k_new, v_new, ring_k, ring_v, ring_lens, stream)
 
 
 def decode_workspace_size(cfg: Config, batch: int, num_q_heads: int, max_seq_len: int,

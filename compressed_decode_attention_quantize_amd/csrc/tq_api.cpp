@@ -64,6 +64,63 @@ TQ_EXPORT tq_status tq_quantize_append(const tq_config *cfg, int layer_idx, cons
   return TQ_OK;
 }
 
+TQ_EXPORT tq_status tq_ring_flush(const tq_config *cfg, int layer_idx, const uint16_t *ring_k, const uint16_t *ring_v,
+                                  int ring_cap, int32_t *ring_lens, int32_t *seq_lens, const int32_t *block_tables,
+                                  int max_blocks_per_seq, int batch, int num_kv_heads, uint8_t *kv_pool,
+                                  int64_t num_blocks, int block_size, void *stream) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (batch < 0 || ring_cap <= 0 || num_kv_heads <= 0 || num_blocks < 0 || block_size <= 0 || max_blocks_per_seq < 0)
+    return fail(TQ_ERR_INVALID_ARG,
+                "tq_ring_flush: need batch >= 0, ring_cap > 0, num_kv_heads > 0, block_size > 0, non-negative sizes");
+  if (batch == 0) return TQ_OK;
+  if (!ring_k || !ring_v || !ring_lens || !seq_lens || !block_tables || !kv_pool)
+    return fail(TQ_ERR_INVALID_ARG, "tq_ring_flush: NULL pointer");
+  if (!aligned16(ring_k) || !aligned16(ring_v) || !aligned16(kv_pool))
+    return fail(TQ_ERR_INVALID_ARG, "tq_ring_flush: ring_k, ring_v and kv_pool must be 16-byte aligned");
+  QuantParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.k = ring_k;
+  p.v = ring_v;
+  p.pool = kv_pool;
+  p.num_tokens = static_cast<int64_t>(batch) * ring_cap;
+  p.total_slots = num_blocks * block_size;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.slot_bytes = cfg->slot_size_aligned;
+  p.key_bytes = cfg->key_packed_size;
+  layer_sign_mask(*cfg, layer_idx, p.sign_words);
+  for (int i = 0; i < 15; ++i) p.midpoints[i] = cfg->midpoints[i];
+  p.sqrt_block = static_cast<float>(std::sqrt(static_cast<double>(cfg->wht_block)));
+  p.ring_lens = ring_lens;
+  p.seq_lens = seq_lens;
+  p.block_tables = block_tables;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.ring_cap = ring_cap;
+  int err = launch_quantize(*cfg, TQ_BF16, p, stream);
+  if (err != hipSuccess) return hip_fail("tq_ring_flush launch", err);
+  err = launch_ring_commit(ring_lens, seq_lens, batch, ring_cap, stream);
+  if (err != hipSuccess) return hip_fail("tq_ring_flush commit launch", err);
+  return TQ_OK;
+}
+
+TQ_EXPORT tq_status tq_ring_append(const tq_config *cfg, const uint16_t *k_new, const uint16_t *v_new, int batch,
+                                   int num_kv_heads, uint16_t *ring_k, uint16_t *ring_v, int ring_cap,
+                                   int32_t *ring_lens, void *stream) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (batch < 0 || ring_cap <= 0 || num_kv_heads <= 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_ring_append: need batch >= 0, ring_cap > 0 and num_kv_heads > 0");
+  if (batch == 0) return TQ_OK;
+  if (!k_new || !v_new || !ring_k || !ring_v || !ring_lens) return fail(TQ_ERR_INVALID_ARG, "tq_ring_append: NULL pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(ring_k) || !aligned16(ring_v))
+    return fail(TQ_ERR_INVALID_ARG, "tq_ring_append: k_new, v_new, ring_k and ring_v must be 16-byte aligned");
+  const int err = launch_ring_append(k_new, v_new, ring_k, ring_v, ring_lens, batch, num_kv_heads, cfg->head_dim,
+                                     ring_cap, stream);
+  if (err != hipSuccess) return hip_fail("tq_ring_append launch", err);
+  return TQ_OK;
+}
+
 TQ_EXPORT tq_status tq_dequant(const tq_config *cfg, int layer_idx, const uint8_t *kv_pool, int64_t num_blocks,
                                int num_kv_heads, int block_size, const int64_t *slot_ids, int64_t n,
                                float *k_out, float *v_out, void *stream) {

@@ -249,6 +249,44 @@ TQ_EXPORT tq_status tq_layer_config(const tq_config *base, int layer_idx, int in
   return TQ_OK;
 }
 
+TQ_EXPORT int tq_boundary_skip_layers(int num_layers, int n, int hybrid, int32_t *out, int out_cap) {
+  if (out_cap < 0 || (out_cap > 0 && !out)) {
+    fail(TQ_ERR_INVALID_ARG, "tq_boundary_skip_layers: out is NULL or out_cap < 0");
+    return -1;
+  }
+  clear_error();
+  if (hybrid || n <= 0 || num_layers <= 0) return 0;
+  n = std::min(n, num_layers / 2);
+  // first n, then last n, skipping the overlap (num_layers <= 2 n cannot
+  // happen after the cap, but the loop keeps indices unique either way)
+  int count = 0;
+  for (int i = 0; i < num_layers; ++i) {
+    if (i < n || i >= num_layers - n) {
+      if (count < out_cap) out[count] = i;
+      ++count;
+    }
+  }
+  return count;
+}
+
+TQ_EXPORT int64_t tq_attn_page_size_1_token(const tq_config *cfg, int num_kv_heads, int skip_dtype_bytes) {
+  if (check_config(cfg) != TQ_OK) return -1;
+  if (num_kv_heads <= 0 || skip_dtype_bytes < 0) {
+    fail(TQ_ERR_INVALID_ARG, "tq_attn_page_size_1_token: num_kv_heads must be positive, skip_dtype_bytes >= 0");
+    return -1;
+  }
+  const int64_t tq = static_cast<int64_t>(num_kv_heads) * cfg->slot_size_aligned;
+  if (skip_dtype_bytes == 0) return tq;
+  const int64_t skip = 2ll * num_kv_heads * cfg->head_dim * skip_dtype_bytes;
+  int64_t a = tq, b = skip;
+  while (b) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return tq / a * skip;
+}
+
 TQ_EXPORT int32_t tq_slot_size(const tq_config *cfg, int aligned) {
   if (check_config(cfg) != TQ_OK) return -1;
   return aligned ? cfg->slot_size_aligned : cfg->slot_size;

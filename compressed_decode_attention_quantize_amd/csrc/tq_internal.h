@@ -40,6 +40,16 @@ struct QuantParams {
   uint32_t sign_words[4];
   float midpoints[15];
   float sqrt_block;     // fp32(sqrt(B))
+  // Ring flush mode (ring_lens != nullptr): token n is ring position
+  // n % ring_cap of sequence n / ring_cap, read at
+  // (seq * num_kv_heads + h) * ring_cap * D + pos * D; it is written only if
+  // that sequence's ring is full, at position seq_lens[seq] + pos through its
+  // block table. slot_mapping, k_stride and v_stride are unused.
+  const int32_t *ring_lens;
+  const int32_t *seq_lens;
+  const int32_t *block_tables;
+  int32_t max_blocks_per_seq;
+  int32_t ring_cap;
 };
 
 struct DequantParams {
@@ -94,6 +104,9 @@ struct DecodeParams {
 // HIP error code as int.
 int launch_quantize(const tq_config &cfg, tq_dtype dtype, const QuantParams &p, void *stream);
 int launch_dequant(const tq_config &cfg, const DequantParams &p, void *stream);
+int launch_ring_commit(int32_t *ring_lens, int32_t *seq_lens, int batch, int ring_cap, void *stream);
+int launch_ring_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *ring_k, uint16_t *ring_v,
+                       int32_t *ring_lens, int batch, int num_kv_heads, int head_dim, int ring_cap, void *stream);
 int launch_decode(const tq_config &cfg, tq_dtype q_dtype, const DecodeParams &p, void *stream);
 
 // Split plan shared by tq_decode_workspace_size and tq_decode_attention.

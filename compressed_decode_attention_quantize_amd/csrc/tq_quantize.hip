@@ -66,15 +66,35 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   const int64_t t = active ? vec / p.num_kv_heads : 0;
   const int h = active ? static_cast<int>(vec - t * p.num_kv_heads) : 0;
 
+  // source element offsets of this (token, head) row, and its slot
+  int64_t k_off, v_off, slot = -1;
+  if (p.ring_lens) {
+    const int64_t seq = t / p.ring_cap;
+    const int pos = static_cast<int>(t - seq * p.ring_cap);
+    k_off = v_off = ((seq * p.num_kv_heads + h) * p.ring_cap + pos) * D;
+    if (active && p.ring_lens[seq] >= p.ring_cap) {
+      const int64_t at = static_cast<int64_t>(max(p.seq_lens[seq], 0)) + pos;
+      const int64_t lblk = at / p.block_size;
+      if (lblk < p.max_blocks_per_seq) {
+        const int64_t phys = p.block_tables[seq * p.max_blocks_per_seq + lblk];
+        if (phys >= 0) slot = phys * p.block_size + (at - lblk * p.block_size);
+      }
+    }
+  } else {
+    k_off = t * p.k_stride + static_cast<int64_t>(h) * D;
+    v_off = t * p.v_stride + static_cast<int64_t>(h) * D;
+    if (active) slot = p.slot_mapping[t];
+  }
   float x[8], v[8];
-  if (active) {
-    load8<DT>(p.k, t * p.k_stride + static_cast<int64_t>(h) * D + 8 * r, x);
-    load8<DT>(p.v, t * p.v_stride + static_cast<int64_t>(h) * D + 8 * r, v);
+  // a ring that is not full is not read (its team computes on zeros and
+  // writes nothing); a team shares its token, so this is uniform per team
+  if (active && (p.ring_lens == nullptr || slot >= 0)) {
+    load8<DT>(p.k, k_off + 8 * r, x);
+    load8<DT>(p.v, v_off + 8 * r, v);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = v[i] = 0.0f;
   }
-  int64_t slot = active ? p.slot_mapping[t] : -1;
   const bool write = active && slot >= 0 && slot < p.total_slots;
   if (!write) slot = 0;
   const int64_t blk = slot / p.block_size;
@@ -223,6 +243,40 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantParams p) {
   vo[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// After a ring flush: every full ring's tokens are now compressed positions,
+// so its sequence grows by ring_cap and the ring empties.
+__global__ void ring_commit_kernel(int32_t *ring_lens, int32_t *seq_lens, int batch, int ring_cap) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch && ring_lens[b] >= ring_cap) {
+    seq_lens[b] = max(seq_lens[b], 0) + ring_cap;
+    ring_lens[b] = 0;
+  }
+}
+
+// One workgroup per sequence: its new token's K and V rows (bf16, 8 elements
+// per thread and step) go to ring position ring_lens[b], which then grows by
+// one. A full ring is left as it is.
+__global__ __launch_bounds__(kThreads) void ring_append_kernel(const uint16_t *k_new, const uint16_t *v_new,
+                                                                 uint16_t *ring_k, uint16_t *ring_v,
+                                                                 int32_t *ring_lens, int num_kv_heads,
+                                                                 int head_dim, int ring_cap) {
+  const int b = blockIdx.x;
+  const int r = ring_lens[b];
+  const bool room = r >= 0 && r < ring_cap;
+  if (room) {
+    const int vecs = num_kv_heads * head_dim / 8;
+    for (int i = threadIdx.x; i < vecs; i += blockDim.x) {
+      const int h = (i * 8) / head_dim, j = i * 8 - h * head_dim;
+      const int64_t src = (static_cast<int64_t>(b) * num_kv_heads + h) * head_dim + j;
+      const int64_t dst = ((static_cast<int64_t>(b) * num_kv_heads + h) * ring_cap + r) * head_dim + j;
+      *reinterpret_cast<uint4 *>(ring_k + dst) = *reinterpret_cast<const uint4 *>(k_new + src);
+      *reinterpret_cast<uint4 *>(ring_v + dst) = *reinterpret_cast<const uint4 *>(v_new + src);
+    }
+  }
+  __syncthreads();  // every thread has read ring_lens[b]
+  if (threadIdx.x == 0 && room) ring_lens[b] = r + 1;
+}
+
 template <int D, int KB, int VB>
 int launch_quantize_t(tq_dtype dt, const QuantParams &p, hipStream_t s) {
   using T = Team<D>;
@@ -292,6 +346,19 @@ int launch_quantize(const tq_config &c, tq_dtype dt, const QuantParams &p, void 
     case 128: return dispatch_quantize_bits<128>(c, dt, p, s);
   }
   return hipErrorInvalidValue;
+}
+
+int launch_ring_commit(int32_t *ring_lens, int32_t *seq_lens, int batch, int ring_cap, void *stream) {
+  hipLaunchKernelGGL(ring_commit_kernel, dim3((batch + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     ring_lens, seq_lens, batch, ring_cap);
+  return hipGetLastError();
+}
+
+int launch_ring_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *ring_k, uint16_t *ring_v,
+                       int32_t *ring_lens, int batch, int num_kv_heads, int head_dim, int ring_cap, void *stream) {
+  hipLaunchKernelGGL(ring_append_kernel, dim3(batch), dim3(kThreads), 0, static_cast<hipStream_t>(stream), k_new, v_new,
+                     ring_k, ring_v, ring_lens, num_kv_heads, head_dim, ring_cap);
+  return hipGetLastError();
 }
 
 int launch_dequant(const tq_config &c, const DequantParams &p, void *stream) {

@@ -19,6 +19,9 @@
  *         direction 2 (2-bit values beside 4-bit ones) and direction 3
  *         (initial_layers_key_bits: the first four layers get one more key
  *         bit).
+ *  [PR]   also: implementation item 1 (hybrid models skip no layers) and
+ *         the interface.py snippet (per-token attention page = lcm of the
+ *         TurboQuant page and the unquantized skip-layer page).
  *
  * Conventions for every function:
  *  - Returns a tq_status; never throws or aborts. On failure nothing is
@@ -129,6 +132,24 @@ tq_status tq_config_from_preset(const char *preset, int head_dim, tq_config *out
 tq_status tq_layer_config(const tq_config *base, int layer_idx, int initial_layers,
                           int initial_layers_key_bits, tq_config *out);
 
+/* Boundary protection ([API] get_boundary_skip_layers): the layers that keep
+ * the unquantized cache, ascending: the first n and the last n of a dense
+ * model, n capped at num_layers / 2, each index once; none when n <= 0,
+ * num_layers <= 0, or hybrid != 0 ([PR] item 1). Writes at most out_cap
+ * indices to out and returns how many there are (the caller can size out
+ * from a first call with out_cap = 0); -1 if out is NULL with out_cap > 0.
+ * Host only. */
+int tq_boundary_skip_layers(int num_layers, int n, int hybrid, int32_t *out, int out_cap);
+
+/* Per-token page bytes every attention layer shares ([PR] interface.py):
+ * the TurboQuant page num_kv_heads * slot_size_aligned, or, when skip layers
+ * exist (skip_dtype_bytes > 0, the element size of their unquantized cache),
+ * lcm(that, 2 * num_kv_heads * head_dim * skip_dtype_bytes): the least
+ * common multiple, not the maximum, so both page kinds tile it. The skip
+ * page formula (K and V rows of every head) is this library's reading.
+ * Returns < 0 on invalid input. Host only. */
+int64_t tq_attn_page_size_1_token(const tq_config *cfg, int num_kv_heads, int skip_dtype_bytes);
+
 /* Slot bytes per head per position ([API] slot_size / slot_size_aligned):
  * aligned != 0 gives slot_size_aligned. Returns < 0 on a null or invalid
  * config. Host only. */
@@ -171,6 +192,47 @@ tq_status tq_quantize_append(const tq_config *cfg, int layer_idx,
                              const int64_t *slot_mapping,
                              uint8_t *kv_pool, int64_t num_blocks, int block_size,
                              void *stream);
+
+/*
+ * Ring flush ([ART] write path: decode tokens wait in a bf16 ring that is
+ * compressed as one whole chunk when it overflows). For every sequence b whose
+ * ring is full (ring_lens[b] >= ring_cap), its ring tokens 0..ring_cap-1 are
+ * quantize-appended, exactly as tq_quantize_append would, at sequence
+ * positions seq_lens[b] .. seq_lens[b] + ring_cap - 1 (slot
+ * block_tables[b][p / block_size] * block_size + p % block_size); then
+ * seq_lens[b] += ring_cap and ring_lens[b] = 0. Other sequences are left
+ * alone. Everything runs on the device, in stream order, with no host sync:
+ * a decode step calls tq_ring_flush, then tq_ring_append, then
+ * tq_decode_attention.
+ *
+ *  ring_k/ring_v device bf16 [batch][num_kv_heads][ring_cap][head_dim],
+ *                16-byte aligned (the layout tq_decode_attention reads).
+ *  ring_lens, seq_lens   device int32 [batch], updated in place.
+ *  block_tables  device int32 [batch][max_blocks_per_seq]; the caller has
+ *                allocated the blocks the flushed positions fall in.
+ *                Positions past max_blocks_per_seq, and negative or
+ *                out-of-range block ids, are not written.
+ *  kv_pool       device, 16-byte aligned, as for tq_quantize_append.
+ */
+tq_status tq_ring_flush(const tq_config *cfg, int layer_idx,
+                        const uint16_t *ring_k, const uint16_t *ring_v, int ring_cap,
+                        int32_t *ring_lens, int32_t *seq_lens,
+                        const int32_t *block_tables, int max_blocks_per_seq,
+                        int batch, int num_kv_heads,
+                        uint8_t *kv_pool, int64_t num_blocks, int block_size,
+                        void *stream);
+
+/*
+ * Ring append ([ART] write path): each sequence's new decode token, k_new /
+ * v_new device bf16 [batch][num_kv_heads][head_dim] (16-byte aligned), is
+ * copied to ring position ring_lens[b], which then grows by one. A full ring
+ * (ring_lens[b] >= ring_cap) is left unchanged and that token is not
+ * stored: flush first. Runs on the device, no host sync.
+ */
+tq_status tq_ring_append(const tq_config *cfg, const uint16_t *k_new, const uint16_t *v_new,
+                         int batch, int num_kv_heads,
+                         uint16_t *ring_k, uint16_t *ring_v, int ring_cap, int32_t *ring_lens,
+                         void *stream);
 
 /*
  * Workspace bytes for tq_decode_attention with the same arguments. The

@@ -197,3 +197,36 @@ def test_workspace_size_and_plan():
     # the header grows with the batch (tile prefix per sequence)
     b, _ = tq.decode_workspace_size(c, 100, 8, 100, 0, 0)
     assert b == 512 + 100 * 8 * 2 * 132 * 4
+
+
+@pytest.mark.parametrize("num_layers", [0, 1, 2, 3, 4, 5, 10, 28, 32, 61])
+@pytest.mark.parametrize("n", [-1, 0, 1, 2, 3, 40])
+def test_boundary_skip_layers_match_oracle(num_layers, n):
+    from oracle import cache as OCache
+    assert tq.boundary_skip_layers(num_layers, n) == OCache.boundary_skip_layers(num_layers, n)
+    assert tq.boundary_skip_layers(num_layers, n, hybrid=True) == []
+
+
+@pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("d,hkv", [(64, 2), (96, 4), (128, 8)])
+@pytest.mark.parametrize("skip_bytes", [0, 1, 2, 4])
+def test_attn_page_size_matches_oracle(preset, d, hkv, skip_bytes):
+    from oracle import cache as OCache
+    assert tq.attn_page_size_1_token(tq.config_from_preset(preset, d), hkv, skip_bytes) == \
+        OCache.attn_page_bytes_1_token(OC.from_cache_dtype(preset, d), hkv, skip_bytes)
+
+
+def test_ring_argument_errors_before_launch():
+    c = tq.config_from_preset("turboquant_3bit_nc", 128)
+    buf = ctypes.create_string_buffer(4096 + 16)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    cfgp = ctypes.byref(c)
+    # flush: ring_cap 0, NULL ring_lens, misaligned pool; batch 0 is a no-op
+    assert _c_call("tq_ring_flush", cfgp, 0, al, al, 0, al, al, al, 4, 2, 8, al, 10, 16, None) == 1
+    assert _c_call("tq_ring_flush", cfgp, 0, al, al, 128, None, al, al, 4, 2, 8, al, 10, 16, None) == 1
+    assert _c_call("tq_ring_flush", cfgp, 0, al, al, 128, al, al, al, 4, 2, 8, al + 2, 10, 16, None) == 1
+    assert _c_call("tq_ring_flush", cfgp, 0, None, None, 128, None, None, None, 4, 0, 8, None, 10, 16, None) == 0
+    # append: NULL k_new, misaligned ring; batch 0 is a no-op
+    assert _c_call("tq_ring_append", cfgp, None, al, 2, 8, al, al, 128, al, None) == 1
+    assert _c_call("tq_ring_append", cfgp, al, al, 2, 8, al + 4, al, 128, al, None) == 1
+    assert _c_call("tq_ring_append", cfgp, None, None, 0, 8, None, None, 128, None, None) == 0
