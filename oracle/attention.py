@@ -24,6 +24,13 @@ head g // G; ring tokens are exact bf16 keys/values attended with the raw
 (unrotated) query; a sequence with no tokens outputs zeros; the output is
 float64 here and fp32 in the library.
 
+Continuation prefill (``prefill_attention``): the API page keeps the
+centroid table even for FP8 keys because continuation prefill dequantizes
+the cache (``mse_bits`` docstring). Reading: a new chunk of C tokens of a
+sequence with L compressed tokens attends, token t of the chunk, to the L
+dequantized history tokens and to the chunk's own exact tokens 0..t
+(causal), with the same scale and GQA mapping as decode.
+
 ``rotated_scores`` computes the fused kernel's form
 n16 * <Pi q, c> (c re-normalized under norm correction) and
 ``tests/test_oracle_attention.py`` checks it equals q . k_hat to 1e-12.
@@ -99,3 +106,28 @@ def rotated_scores(q_row, slots, cfg: TQConfig, layer_idx: int) -> np.ndarray:
     if cfg.norm_correction:
         dots = dots / np.linalg.norm(y, axis=1)
     return codec.f16_bits_to_f32(f["norm16"]).astype(np.float64) * dots
+
+
+def prefill_attention(q, k_chunk, v_chunk, cu_chunk, pool, block_tables, hist_lens, cfg: TQConfig,
+                      layer_idx: int, scale=None) -> np.ndarray:
+    """q [N, Hq, D], k_chunk / v_chunk [N, Hkv, D] (float values of the exact
+    chunk tokens), cu_chunk [B + 1] (sequence b's chunk is rows
+    cu_chunk[b]..cu_chunk[b+1]-1), hist_lens [B] -> out [N, Hq, D] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    n, hq, d = q.shape
+    hkv = pool.shape[1]
+    grp = hq // hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((n, hq, d), dtype=np.float64)
+    for b in range(len(cu_chunk) - 1):
+        r0, r1 = int(cu_chunk[b]), int(cu_chunk[b + 1])
+        for h in range(hkv):
+            kh, vh = sequence_kv(pool, block_tables[b], int(hist_lens[b]), h, cfg, layer_idx)
+            kc = np.asarray(k_chunk[r0:r1, h], np.float64)
+            vc = np.asarray(v_chunk[r0:r1, h], np.float64)
+            for t in range(r1 - r0):
+                k = np.concatenate([kh, kc[:t + 1]], axis=0)
+                v = np.concatenate([vh, vc[:t + 1]], axis=0)
+                out[r0 + t, h * grp:(h + 1) * grp] = softmax_attend(q[r0 + t, h * grp:(h + 1) * grp], k, v, scale)
+    return out

@@ -166,3 +166,65 @@ def test_gqa_mapping():
         s = (k @ q[0, g]) / 8.0
         p = np.exp(s - s.max())
         assert np.allclose(out[0, g], (p / p.sum()) @ v, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- continuation prefill
+
+def test_prefill_one_token_chunk_is_decode_with_one_ring_token():
+    """A one-token chunk attends to the history plus itself: exactly decode
+    with that token as the only ring token."""
+    cfg = C.from_cache_dtype("turboquant_k3v4_nc", 96)
+    lens = [37, 0, 16]
+    pool, tables = _fill(cfg, lens, hkv=2, seed=21)
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((3, 4, 96))
+    kc = rng.standard_normal((3, 2, 96))
+    vc = rng.standard_normal((3, 2, 96))
+    got = A.prefill_attention(q, kc, vc, [0, 1, 2, 3], pool, tables, lens, cfg, 1)
+    want = A.decode_attention(q, pool, tables, lens, cfg, 1, ring_k=kc[:, :, None], ring_v=vc[:, :, None],
+                              ring_lens=[1, 1, 1])
+    assert np.array_equal(got, want)
+
+
+def test_prefill_without_history_is_causal_sdpa():
+    """No compressed history: causal attention over the chunk, checked with
+    torch's scaled_dot_product_attention (is_causal) in float64."""
+    cfg = C.from_cache_dtype("turboquant_4bit_nc", 64)
+    pool = np.zeros((1, 2, 16, cfg.slot_size_aligned), np.uint8)
+    rng = np.random.default_rng(23)
+    n = 19
+    q = rng.standard_normal((n, 6, 64))
+    kc = rng.standard_normal((n, 2, 64))
+    vc = rng.standard_normal((n, 2, 64))
+    got = A.prefill_attention(q, kc, vc, [0, n], pool, np.zeros((1, 1), np.int32), [0], cfg, 0, scale=0.2)
+    qq = torch.from_numpy(q).permute(1, 0, 2)                                  # [6, n, 64]
+    kk = torch.from_numpy(kc).permute(1, 0, 2).repeat_interleave(3, dim=0)     # head g -> kv head g // 3
+    vv = torch.from_numpy(vc).permute(1, 0, 2).repeat_interleave(3, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True, scale=0.2)
+    assert np.allclose(got, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_brute_force_tiny():
+    """Two sequences with history and chunks of 3 and 5 tokens: every output
+    row against an explicit loop over the visible keys."""
+    cfg = C.TQConfig(head_dim=64, key_quant_bits=4, value_quant_bits=2, norm_correction=True)
+    lens = [21, 5]
+    pool, tables = _fill(cfg, lens, hkv=1, seed=24)
+    rng = np.random.default_rng(25)
+    cu = [0, 3, 8]
+    q = rng.standard_normal((8, 2, 64))
+    kc = rng.standard_normal((8, 1, 64))
+    vc = rng.standard_normal((8, 1, 64))
+    got = A.prefill_attention(q, kc, vc, cu, pool, tables, lens, cfg, 2)
+    sc = 1 / math.sqrt(64)
+    for b in range(2):
+        kh, vh = A.sequence_kv(pool, tables[b], lens[b], 0, cfg, 2)
+        for t in range(cu[b + 1] - cu[b]):
+            row = cu[b] + t
+            keys = list(kh) + [kc[cu[b] + j, 0] for j in range(t + 1)]
+            vals = list(vh) + [vc[cu[b] + j, 0] for j in range(t + 1)]
+            for g in range(2):
+                s = np.array([sc * float(np.dot(q[row, g], k)) for k in keys])
+                w = np.exp(s - s.max())
+                w /= w.sum()
+                assert np.allclose(got[row, g], sum(wi * vi for wi, vi in zip(w, vals)), rtol=1e-11, atol=1e-12)
