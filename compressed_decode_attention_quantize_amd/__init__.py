@@ -60,6 +60,7 @@ F32, BF16, F16 = 0, 1, 2
 EXPORTED = ["tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_boundary_skip_layers",
             "tq_attn_page_size_1_token", "tq_slot_size", "tq_page_size",
             "tq_layer_signs", "tq_quantize_append", "tq_ring_flush", "tq_ring_append", "tq_decode_workspace_size",
+            "tq_prefill_workspace_size", "tq_prefill_attention",
             "tq_decode_attention", "tq_dequant", "tq_last_error", "tq_version"]
 
 
@@ -106,6 +107,11 @@ _lib.tq_attn_page_size_1_token.restype = _i64
 _lib.tq_ring_flush.argtypes = [_CP, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int, _P, _i64, ctypes.c_int, _P]
 _lib.tq_ring_append.argtypes = [_CP, _P, _P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P]
+_lib.tq_prefill_workspace_size.argtypes = [_CP, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.POINTER(_sz)]
+_lib.tq_prefill_attention.argtypes = [_CP, ctypes.c_int, _P, ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, _P, _i64, ctypes.c_int, _P, ctypes.c_int, _P,
+                                      ctypes.c_int, ctypes.c_float, _P, _P, _sz, _P]
 _lib.tq_slot_size.argtypes = [_CP, ctypes.c_int]
 _lib.tq_slot_size.restype = _i32
 _lib.tq_page_size.argtypes = [_CP, ctypes.c_int, ctypes.c_int]
@@ -121,7 +127,7 @@ _lib.tq_decode_attention.argtypes = [_CP, ctypes.c_int, _P, ctypes.c_int, ctypes
                                      ctypes.c_int, _P]
 _lib.tq_dequant.argtypes = [_CP, ctypes.c_int, _P, _i64, ctypes.c_int, ctypes.c_int, _P, _i64, _P, _P, _P]
 for _name in ("tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_layer_signs", "tq_quantize_append",
-              "tq_ring_flush", "tq_ring_append",
+              "tq_ring_flush", "tq_ring_append", "tq_prefill_workspace_size", "tq_prefill_attention",
               "tq_decode_workspace_size", "tq_decode_attention", "tq_dequant"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.tq_last_error.restype = ctypes.c_char_p
@@ -380,6 +386,56 @@ def decode_attention(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_
                                     block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(),
                                     max_seq_len, rk, rv, rl, ring_cap, float(softmax_scale), out.data_ptr(),
                                     workspace.data_ptr(), workspace.numel(), split_tokens, s))
+    return out
+
+
+def prefill_workspace_size(cfg: Config, batch: int, num_q_heads: int, num_kv_heads: int, max_chunk: int,
+                           max_hist: int, max_blocks_per_seq: int, q_dtype: int = BF16) -> int:
+    n = _sz(0)
+    _check(_lib.tq_prefill_workspace_size(ctypes.byref(cfg), batch, num_q_heads, num_kv_heads, max_chunk, max_hist,
+                                          max_blocks_per_seq, q_dtype, ctypes.byref(n)))
+    return n.value
+
+
+def prefill_attention(cfg: Config, layer_idx: int, q, k_chunk, v_chunk, cu_chunk, max_chunk: int, kv_pool,
+                      block_tables, hist_lens, max_hist: int, softmax_scale: float = 0.0, out=None, workspace=None,
+                      stream=None):
+    """Continuation prefill: q [N, Hq, D] (f32/bf16/f16), k_chunk / v_chunk bf16
+    [N, Hkv, D], cu_chunk int32 [B + 1], hist_lens int32 [B] -> out [N, Hq, D] fp32."""
+    torch = _torch()
+    _dev(q, "q")
+    _dev(k_chunk, "k_chunk", torch.bfloat16)
+    _dev(v_chunk, "v_chunk", torch.bfloat16)
+    _dev(cu_chunk, "cu_chunk", torch.int32)
+    _dev(hist_lens, "hist_lens", torch.int32)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(kv_pool, "kv_pool", torch.uint8)
+    if q.dim() != 3 or q.shape[2] != cfg.head_dim or not q.is_contiguous():
+        raise ValueError(f"q must be contiguous [N, Hq, {cfg.head_dim}]")
+    n, hq, d = q.shape
+    hkv = kv_pool.shape[1]
+    if k_chunk.shape != (n, hkv, d) or v_chunk.shape != k_chunk.shape or not k_chunk.is_contiguous() \
+            or not v_chunk.is_contiguous():
+        raise ValueError(f"k_chunk/v_chunk must be contiguous bf16 [N, {hkv}, {d}]")
+    bsz = hist_lens.shape[0]
+    if cu_chunk.shape != (bsz + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != bsz \
+            or not block_tables.is_contiguous():
+        raise ValueError("cu_chunk must be [B + 1], hist_lens [B], block_tables contiguous [B, max_blocks]")
+    if kv_pool.dim() != 4 or kv_pool.shape[3] != cfg.slot_size_aligned or not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be contiguous [num_blocks, Hkv, block_size, slot_size_aligned]")
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    need = prefill_workspace_size(cfg, bsz, hq, hkv, max_chunk, max_hist, block_tables.shape[1], _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    s = stream if stream is not None else _stream_ptr(q)
+    _check(_lib.tq_prefill_attention(ctypes.byref(cfg), layer_idx, q.data_ptr(), _dtype_code(q), k_chunk.data_ptr(),
+                                     v_chunk.data_ptr(), cu_chunk.data_ptr(), bsz, max_chunk, hq, hkv,
+                                     kv_pool.data_ptr(), kv_pool.shape[0], kv_pool.shape[2], block_tables.data_ptr(),
+                                     block_tables.shape[1], hist_lens.data_ptr(), max_hist, float(softmax_scale),
+                                     out.data_ptr(), workspace.data_ptr(), workspace.numel(), s))
     return out
 
 

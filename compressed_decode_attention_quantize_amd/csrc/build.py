@@ -21,7 +21,7 @@ PKG = os.path.dirname(HERE)
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_quantize.hip", "tq_decode.hip"]
+SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_quantize.hip", "tq_decode.hip", "tq_prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

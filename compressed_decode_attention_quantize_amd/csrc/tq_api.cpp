@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -118,6 +119,172 @@ TQ_EXPORT tq_status tq_ring_append(const tq_config *cfg, const uint16_t *k_new, 
   const int err = launch_ring_append(k_new, v_new, ring_k, ring_v, ring_lens, batch, num_kv_heads, cfg->head_dim,
                                      ring_cap, stream);
   if (err != hipSuccess) return hip_fail("tq_ring_append launch", err);
+  return TQ_OK;
+}
+
+namespace {
+
+// Workspace layout of a continuation prefill (offsets aligned to 256 bytes).
+struct PrefillLayout {
+  int row_groups = 0, vbatch = 0, split_tokens = 0;
+  size_t vq = 0, vtables = 0, vseq = 0, vring = 0, rows = 0, ring_k = 0, ring_v = 0, vout = 0, dec = 0, total = 0;
+  SplitPlan plan;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+tq_status prefill_layout(const tq_config &cfg, int batch, int num_q_heads, int num_kv_heads, int max_chunk,
+                         int max_hist, int max_blocks, int q_elem_bytes, PrefillLayout *L) {
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t rg = (static_cast<int64_t>(max_chunk) * group + 15) / 16;
+  const int64_t vb = static_cast<int64_t>(batch) * rg;
+  if (vb > 8192)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_prefill: batch * ceil(max_chunk * group / 16) must be at most 8192 "
+                                    "(split the chunk)");
+  L->row_groups = static_cast<int>(rg);
+  L->vbatch = static_cast<int>(vb);
+  // a wave covers at least a quarter of the longest history: few partial slots
+  L->split_tokens = std::max(256, (max_hist / 4 + 15) / 16 * 16);
+  const int hq = num_kv_heads * 16;
+  const int d = cfg.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L->vq = take(static_cast<size_t>(vb) * hq * d * q_elem_bytes);
+  L->vtables = take(static_cast<size_t>(vb) * std::max(max_blocks, 1) * 4);
+  L->vseq = take(static_cast<size_t>(vb) * 4);
+  L->vring = take(static_cast<size_t>(vb) * 4);
+  L->rows = take(static_cast<size_t>(vb) * hq * 4);
+  L->ring_k = take(static_cast<size_t>(batch) * num_kv_heads * max_chunk * d * 2);
+  L->ring_v = take(static_cast<size_t>(batch) * num_kv_heads * max_chunk * d * 2);
+  L->vout = take(static_cast<size_t>(vb) * hq * d * 4);
+  const tq_status st = plan_decode(cfg, L->vbatch, hq, max_hist, max_chunk, L->split_tokens, &L->plan);
+  if (st != TQ_OK) return st;
+  L->dec = take(L->plan.workspace_bytes);
+  L->total = off;
+  return TQ_OK;
+}
+
+int dtype_bytes(tq_dtype d) { return d == TQ_F32 ? 4 : 2; }
+
+}  // namespace
+
+TQ_EXPORT tq_status tq_prefill_workspace_size(const tq_config *cfg, int batch, int num_q_heads, int num_kv_heads,
+                                              int max_chunk, int max_hist, int max_blocks_per_seq,
+                                              tq_dtype q_dtype, size_t *bytes_out) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (!bytes_out) return fail(TQ_ERR_INVALID_ARG, "tq_prefill_workspace_size: bytes_out is NULL");
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_chunk < 0 ||
+      max_hist < 0 || max_blocks_per_seq < 0 || !valid_dtype(q_dtype))
+    return fail(TQ_ERR_INVALID_ARG, "tq_prefill_workspace_size: invalid sizes or dtype");
+  PrefillLayout L;
+  st = prefill_layout(*cfg, batch, num_q_heads, num_kv_heads, max_chunk, max_hist, max_blocks_per_seq,
+                      dtype_bytes(q_dtype), &L);
+  if (st != TQ_OK) return st;
+  *bytes_out = L.total;
+  return TQ_OK;
+}
+
+TQ_EXPORT tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx, const void *q, tq_dtype q_dtype,
+                                         const uint16_t *k_chunk, const uint16_t *v_chunk, const int32_t *cu_chunk,
+                                         int batch, int max_chunk, int num_q_heads, int num_kv_heads,
+                                         const uint8_t *kv_pool, int64_t num_blocks, int block_size,
+                                         const int32_t *block_tables, int max_blocks_per_seq,
+                                         const int32_t *hist_lens, int max_hist, float softmax_scale, float *out,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+  tq_status st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (batch < 0 || max_chunk < 0 || max_hist < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_prefill_attention: invalid sizes (num_q_heads must be a multiple of num_kv_heads)");
+  if (block_size <= 0 || block_size % 16 != 0)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_prefill_attention: block_size must be a positive multiple of 16");
+  if (!valid_dtype(q_dtype)) return fail(TQ_ERR_INVALID_ARG, "tq_prefill_attention: unknown q dtype");
+  if (batch == 0 || max_chunk == 0) return TQ_OK;
+  if (!q || !k_chunk || !v_chunk || !cu_chunk || !kv_pool || !block_tables || !hist_lens || !out)
+    return fail(TQ_ERR_INVALID_ARG, "tq_prefill_attention: NULL pointer");
+  if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(kv_pool) || !aligned16(out))
+    return fail(TQ_ERR_INVALID_ARG, "tq_prefill_attention: q, k_chunk, v_chunk, kv_pool and out must be 16-byte aligned");
+  PrefillLayout L;
+  st = prefill_layout(*cfg, batch, num_q_heads, num_kv_heads, max_chunk, max_hist, max_blocks_per_seq,
+                      dtype_bytes(q_dtype), &L);
+  if (st != TQ_OK) return st;
+  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(TQ_ERR_WORKSPACE, "tq_prefill_attention: workspace must be 256-byte aligned and hold " +
+                                      std::to_string(L.total) + " bytes");
+  char *ws = static_cast<char *>(workspace);
+  PrefillParams pp;
+  std::memset(&pp, 0, sizeof(pp));
+  pp.q = q;
+  pp.k_chunk = k_chunk;
+  pp.v_chunk = v_chunk;
+  pp.cu_chunk = cu_chunk;
+  pp.hist_lens = hist_lens;
+  pp.block_tables = block_tables;
+  pp.out = out;
+  pp.vq = ws + L.vq;
+  pp.vtables = reinterpret_cast<int32_t *>(ws + L.vtables);
+  pp.vseq_lens = reinterpret_cast<int32_t *>(ws + L.vseq);
+  pp.vring_lens = reinterpret_cast<int32_t *>(ws + L.vring);
+  pp.row_lens = reinterpret_cast<int32_t *>(ws + L.rows);
+  pp.ring_k = reinterpret_cast<uint16_t *>(ws + L.ring_k);
+  pp.ring_v = reinterpret_cast<uint16_t *>(ws + L.ring_v);
+  pp.vout = reinterpret_cast<float *>(ws + L.vout);
+  pp.q_elem_bytes = dtype_bytes(q_dtype);
+  pp.batch = batch;
+  pp.vbatch = L.vbatch;
+  pp.row_groups = L.row_groups;
+  pp.group = num_q_heads / num_kv_heads;
+  pp.num_q_heads = num_q_heads;
+  pp.num_kv_heads = num_kv_heads;
+  pp.head_dim = cfg->head_dim;
+  pp.max_chunk = max_chunk;
+  pp.max_blocks_per_seq = max_blocks_per_seq;
+  int err = launch_prefill_prep(pp, stream);
+  if (err != hipSuccess) return hip_fail("tq_prefill_attention layout launch", err);
+
+  DecodeParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = pp.vq;
+  p.pool = kv_pool;
+  p.block_tables = pp.vtables;
+  p.seq_lens = pp.vseq_lens;
+  p.ring_k = pp.ring_k;
+  p.ring_v = pp.ring_v;
+  p.ring_lens = pp.vring_lens;
+  p.out = pp.vout;
+  p.num_blocks = num_blocks;
+  p.batch = L.vbatch;
+  p.num_q_heads = num_kv_heads * 16;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_seq_len = max_hist;
+  p.ring_cap = max_chunk;
+  p.split_tokens = L.plan.split_tokens;
+  p.max_splits = L.plan.max_splits;
+  p.splits_total = L.plan.splits_total;
+  p.plan = reinterpret_cast<int32_t *>(ws + L.dec);
+  p.partials = reinterpret_cast<float *>(ws + L.dec + L.plan.header_bytes);
+  p.slot_bytes = cfg->slot_size_aligned;
+  p.key_bytes = cfg->key_packed_size;
+  p.norm_correction = cfg->norm_correction;
+  const float scale = softmax_scale > 0.0f ? softmax_scale
+                                           : static_cast<float>(1.0 / std::sqrt(static_cast<double>(cfg->head_dim)));
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.centroid_scale = cfg->centroid_scale;
+  layer_sign_mask(*cfg, layer_idx, p.sign_words);
+  for (int i = 0; i < 16; ++i) p.centroids[i] = cfg->centroids[i];
+  p.ring_group = L.row_groups;
+  p.ring_row_lens = pp.row_lens;
+  err = launch_decode(*cfg, q_dtype, p, stream);
+  if (err != hipSuccess) return hip_fail("tq_prefill_attention attention launch", err);
+  err = launch_prefill_scatter(pp, stream);
+  if (err != hipSuccess) return hip_fail("tq_prefill_attention scatter launch", err);
   return TQ_OK;
 }
 

@@ -916,7 +916,8 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
     const int g = e / D, j = e - (e / D) * D;
     q_s[g][j] = load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + j);
   }
-  const int64_t ring0 = ((static_cast<int64_t>(b) * p.num_kv_heads + h) * p.ring_cap + c0) * D;
+  const int rb = p.ring_group > 0 ? b / p.ring_group : b;  // the ring this sequence reads
+  const int64_t ring0 = ((static_cast<int64_t>(rb) * p.num_kv_heads + h) * p.ring_cap + c0) * D;
   for (int e = tid; e < kRingChunk * kVec; e += kRingThreads) {
     const int t = e % kRingChunk, c = e / kRingChunk;
     u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
@@ -964,7 +965,11 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
 #pragma unroll
     for (int i = 0; i < kScoreHeads; ++i) {
       const int g = sg + kScoreGroups * i;
-      if (g < G) p_s[g][t] = t < n ? dot[i] * p.scale_log2 : -INFINITY;
+      if (g < G) {
+        // a per-row limit (causal rows of a prefill chunk) cuts the chunk further
+        const int ng = p.ring_row_lens ? min(n, max(p.ring_row_lens[part0 + g] - c0, 0)) : n;
+        p_s[g][t] = t < ng ? dot[i] * p.scale_log2 : -INFINITY;
+      }
     }
   }
   __syncthreads();

@@ -98,10 +98,48 @@ struct DecodeParams {
   float centroid_scale;    // sigma of the f16 centroid table
   uint32_t sign_words[4];
   float centroids[16];
+  // Shared rings (continuation prefill): sequences b .. b + ring_group - 1
+  // read ring b / ring_group (0: each sequence its own ring), and query head
+  // g of sequence b sees only ring tokens < ring_row_lens[b * Hq + g]
+  // (nullable: all of ring_lens[b]).
+  int32_t ring_group;
+  const int32_t *ring_row_lens;
 };
 
 // Launchers (defined in the kernel translation units). Return hipSuccess or a
 // HIP error code as int.
+// Continuation prefill: the chunk's query rows regrouped as virtual decode
+// sequences of 16 rows per KV head (workspace views in the lower half).
+struct PrefillParams {
+  const void *q;
+  const uint16_t *k_chunk;
+  const uint16_t *v_chunk;
+  const int32_t *cu_chunk;
+  const int32_t *hist_lens;
+  const int32_t *block_tables;
+  float *out;
+  void *vq;             // [vbatch][Hkv * 16][D], q's dtype
+  int32_t *vtables;     // [vbatch][max_blocks_per_seq]
+  int32_t *vseq_lens;   // [vbatch]
+  int32_t *vring_lens;  // [vbatch]
+  int32_t *row_lens;    // [vbatch][Hkv * 16]
+  uint16_t *ring_k;     // [batch][Hkv][max_chunk][D]
+  uint16_t *ring_v;
+  float *vout;          // [vbatch][Hkv * 16][D]
+  int32_t q_elem_bytes;
+  int32_t batch;
+  int32_t vbatch;       // batch * row_groups
+  int32_t row_groups;   // ceil(max_chunk * group / 16)
+  int32_t group;        // query heads per KV head
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_chunk;
+  int32_t max_blocks_per_seq;
+};
+
+int launch_prefill_prep(const PrefillParams &p, void *stream);
+int launch_prefill_scatter(const PrefillParams &p, void *stream);
 int launch_quantize(const tq_config &cfg, tq_dtype dtype, const QuantParams &p, void *stream);
 int launch_dequant(const tq_config &cfg, const DequantParams &p, void *stream);
 int launch_ring_commit(int32_t *ring_lens, int32_t *seq_lens, int batch, int ring_cap, void *stream);

@@ -235,6 +235,50 @@ tq_status tq_ring_append(const tq_config *cfg, const uint16_t *k_new, const uint
                          void *stream);
 
 /*
+ * Continuation prefill over the compressed cache ([API] mse_bits docstring:
+ * the centroid table is kept for continuation-prefill dequant; computed as
+ * in [ART] direction 1, with the query rotated forward). Sequence b's new
+ * chunk is rows cu_chunk[b] .. cu_chunk[b+1]-1 of q / k_chunk / v_chunk;
+ * row t of it attends to the sequence's hist_lens[b] compressed tokens
+ * (through its block table) and to the chunk's exact tokens 0..t (causal):
+ *
+ *   out[r, g, :] = sum_j softmax_j(scale * q[r, g] . k_j) v_j
+ *
+ * Query head g reads KV head g / (num_q_heads / num_kv_heads). The chunk
+ * rows of one KV head are processed 16 at a time by the decode kernels, so
+ * every 16 (token, head) rows stream the history once.
+ *
+ *  q             device [N][num_q_heads][head_dim], dtype q_dtype, 16-byte
+ *                aligned (N = cu_chunk[batch]).
+ *  k_chunk/v_chunk device bf16 [N][num_kv_heads][head_dim], 16-byte aligned.
+ *  cu_chunk      device int32 [batch + 1], non-decreasing from 0, each chunk
+ *                at most max_chunk rows (host bound).
+ *  hist_lens     device int32 [batch], at most max_hist (host bound).
+ *  kv_pool, block_tables, block_size: as for tq_decode_attention.
+ *  out           device fp32 [N][num_q_heads][head_dim], 16-byte aligned.
+ *  workspace     device, tq_prefill_workspace_size bytes, 256-byte aligned;
+ *                contents on entry do not matter.
+ * batch * ceil(max_chunk * (num_q_heads / num_kv_heads) / 16) may be at most
+ * 8192 (TQ_ERR_UNSUPPORTED otherwise: split the chunk). The chunk itself is
+ * not written to the cache: tq_quantize_append does that.
+ */
+tq_status tq_prefill_workspace_size(const tq_config *cfg, int batch, int num_q_heads, int num_kv_heads,
+                                    int max_chunk, int max_hist, int max_blocks_per_seq,
+                                    tq_dtype q_dtype, size_t *bytes_out);
+
+tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx,
+                               const void *q, tq_dtype q_dtype,
+                               const uint16_t *k_chunk, const uint16_t *v_chunk,
+                               const int32_t *cu_chunk, int batch, int max_chunk,
+                               int num_q_heads, int num_kv_heads,
+                               const uint8_t *kv_pool, int64_t num_blocks, int block_size,
+                               const int32_t *block_tables, int max_blocks_per_seq,
+                               const int32_t *hist_lens, int max_hist,
+                               float softmax_scale, float *out,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
  * Workspace bytes for tq_decode_attention with the same arguments. The
  * decode flattens the batch's (sequence, KV head, 16-token tile) triples and
  * gives every resident wave an equal contiguous range of them, of at least

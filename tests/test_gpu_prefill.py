@@ -1,0 +1,91 @@
+"""GPU parity of continuation prefill over the compressed cache against the
+oracle's float64 definition (history dequantized, chunk exact and causal):
+relative L2 <= 2e-3 per (chunk row, query head)."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as OA
+from tests.gpu_common import ATTN_RTOL, announce, oracle_cfg, oracle_pool, per_head_rel_l2
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+tq = pytest.importorskip("compressed_decode_attention_quantize_amd")
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+CASES = {
+    # name: (d, kb, vb, nc, hq, hkv, hist_lens, chunk_lens, q dtype)
+    "4bit_nc_g4": (128, 4, 4, True, 8, 2, [300, 0], [37, 5], "bf16"),
+    "k3v4_d96_g8": (96, 3, 4, True, 16, 2, [1500, 17], [64, 1], "bf16"),
+    "k8v2_d64_g1": (64, 8, 2, False, 2, 2, [40], [100], "f32"),
+    "3bit_g16_f16": (128, 3, 3, True, 32, 2, [700, 129, 0], [9, 16, 33], "f16"),
+}
+
+
+def _scenario(d, kb, vb, nc, hq, hkv, hist, chunks, qdt, seed):
+    cfg = tq.config_init(d, kb, vb, nc, 42)
+    ocfg = oracle_cfg(cfg)
+    rng = np.random.default_rng(seed)
+    bs = 16
+    B = len(hist)
+    nblk = [max(1, math.ceil(n / bs)) for n in hist]
+    nb = sum(nblk) + 1
+    perm = rng.permutation(nb)
+    tables = np.zeros((B, max(nblk)), np.int32)
+    o = 0
+    ks, vs, maps = [], [], []
+    for b, n in enumerate(hist):
+        tables[b, :nblk[b]] = perm[o:o + nblk[b]]
+        o += nblk[b]
+        k = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        k[:, :, rng.choice(d, 4, replace=False)] *= 10
+        k = torch.from_numpy(k).to(torch.bfloat16).float().numpy()
+        v = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+        pos = np.arange(n)
+        maps.append(tables[b, pos // bs].astype(np.int64) * bs + pos % bs)
+        ks.append(k)
+        vs.append(v)
+    pool = oracle_pool(ocfg, 0, np.concatenate(ks), np.concatenate(vs), np.concatenate(maps), nb, hkv, bs)
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    n = int(cu[-1])
+    q = torch.from_numpy(rng.standard_normal((n, hq, d)).astype(np.float32)).to(DT[qdt])
+    kc = torch.from_numpy(rng.standard_normal((n, hkv, d)).astype(np.float32)).to(torch.bfloat16)
+    vc = torch.from_numpy(rng.standard_normal((n, hkv, d)).astype(np.float32)).to(torch.bfloat16)
+    return cfg, ocfg, pool, tables, cu, q, kc, vc
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prefill_matches_oracle(name):
+    d, kb, vb, nc, hq, hkv, hist, chunks, qdt = CASES[name]
+    announce(f"prefill {name}")
+    cfg, ocfg, pool, tables, cu, q, kc, vc = _scenario(d, kb, vb, nc, hq, hkv, hist, chunks, qdt, sum(name.encode()))
+    out = tq.prefill_attention(cfg, 0, q.cuda(), kc.cuda(), vc.cuda(), torch.from_numpy(cu).cuda(), max(chunks),
+                               torch.from_numpy(pool).cuda(), torch.from_numpy(tables).cuda(),
+                               torch.tensor(hist, dtype=torch.int32).cuda(), max(hist))
+    want = OA.prefill_attention(q.float().numpy(), kc.float().numpy(), vc.float().numpy(), cu, pool, tables, hist,
+                                ocfg, 0)
+    err = per_head_rel_l2(out.cpu().numpy(), want)  # rows x heads
+    announce(f"  rel L2 {err:.2e}")
+    assert err <= ATTN_RTOL
+
+
+def test_prefill_garbage_workspace_and_repeat():
+    """Workspace contents on entry do not matter; repeated calls agree bit for bit."""
+    d, kb, vb, nc, hq, hkv, hist, chunks, qdt = CASES["4bit_nc_g4"]
+    announce("prefill garbage workspace")
+    cfg, ocfg, pool, tables, cu, q, kc, vc = _scenario(d, kb, vb, nc, hq, hkv, hist, chunks, qdt, 5)
+    args = (q.cuda(), kc.cuda(), vc.cuda(), torch.from_numpy(cu).cuda(), max(chunks), torch.from_numpy(pool).cuda(),
+            torch.from_numpy(tables).cuda(), torch.tensor(hist, dtype=torch.int32).cuda(), max(hist))
+    need = tq.prefill_workspace_size(cfg, len(hist), hq, hkv, max(chunks), max(hist), tables.shape[1], tq.BF16)
+    outs = []
+    for fill in (0xff, 0x41, 0x00):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        outs.append(tq.prefill_attention(cfg, 0, *args, workspace=ws).cpu().numpy())
+    assert np.isfinite(outs[0]).all()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
