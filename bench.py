@@ -214,6 +214,142 @@ def concurrent_prefill(built, tq, torch, steps, reps=10):
             "overlapped_GBps": (pbytes + dbytes) / (both_ms / 1e3) / 1e9}
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 matrix peak, published
+
+
+def prefill_flops(w, hist_lens, chunk) -> int:
+    """Dense work of one continuation prefill: per (chunk token, query head),
+    2 D flops for q.k and 2 D for p.v over every visible key (history plus
+    the causal part of the chunk)."""
+    total = 0
+    for L in hist_lens:
+        vis = chunk * int(L) + chunk * (chunk + 1) // 2
+        total += 4 * w.head_dim * w.num_q_heads * vis
+    return total
+
+
+def prefill_cpu_baseline(built, chunk_q, chunk_k, chunk_v, budget_s: float):
+    """The oracle's continuation prefill on host cores: sequence 0's history
+    with the first rows of its chunk, repeated for about budget_s."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as OA
+    from oracle import codec as OX
+    from oracle import config as OC
+
+    w, cfg = built.w, built.cfg
+    ocfg = OC.TQConfig(head_dim=cfg.head_dim, key_quant_bits=cfg.key_quant_bits,
+                       value_quant_bits=cfg.value_quant_bits, seed=int(cfg.seed),
+                       norm_correction=bool(cfg.norm_correction))
+    k, v = built.captured[0]
+    n = k.shape[0]
+    bs = w.block_size
+    nblk = max(1, -(-n // bs))
+    pool = np.zeros((nblk, w.num_kv_heads, bs, ocfg.slot_size_aligned), np.uint8)
+    for s0 in range(0, n, 16384):
+        OX.append(pool, k[s0:s0 + 16384], v[s0:s0 + 16384], np.arange(s0, min(n, s0 + 16384)), ocfg, 0)
+    rows = 8
+    q = chunk_q[:rows].float().cpu().numpy()
+    kc = chunk_k[:rows].float().cpu().numpy()
+    vc = chunk_v[:rows].float().cpu().numpy()
+    table = np.arange(nblk, dtype=np.int32)[None]
+    toks = reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            OA.prefill_attention(q, kc, vc, [0, rows], pool, table, [n], ocfg, 0)
+            toks += rows
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    return {"value": toks / el, "unit": "chunk tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequence 0: {rows} chunk rows over its {n}-token history, {w.num_q_heads} q heads, "
+                      f"{reps}x in {el:.1f} s, numpy single-threaded"}
+
+
+def run_prefill(args, w, tq, torch):
+    """Continuation prefill step: attention of every sequence's new chunk to
+    its compressed history and causally to itself, then quantize-append of the
+    chunk (into spare blocks)."""
+    from workloads import KVSource
+    from workloads import gpu as WG
+
+    spare = w.batch * -(-w.chunk // w.block_size)
+    print(f"[bench] building {w.name}: {w.description}", file=sys.stderr, flush=True)
+    built = WG.build(w, "cuda", n_pools=1, capture=(0,), extra_blocks=spare)
+    n = w.batch * w.chunk
+    src = KVSource(w, "cuda", stream_id=55)
+    ck, cv = src.kv(n)                                   # [n, Hkv, D] bf16
+    cq = KVSource(w, "cuda", stream_id=56).q(n)            # [n, Hq, D] bf16
+    cu = torch.arange(0, n + 1, w.chunk, dtype=torch.int32, device="cuda")
+    out = torch.empty((n, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    need = tq.prefill_workspace_size(built.cfg, w.batch, w.num_q_heads, w.num_kv_heads, w.chunk,
+                                     built.max_seq_len, built.tables.shape[1], tq.BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ids = torch.from_numpy(WG.spare_slot_ids(built, n)).cuda()
+
+    def attn():
+        tq.prefill_attention(built.cfg, 0, cq, ck, cv, cu, w.chunk, built.pools[0], built.tables, built.seq_lens,
+                             built.max_seq_len, out=out, workspace=ws)
+
+    append = tq.prepare_quantize(built.cfg, 0, ck, cv, ids, built.pools[0])
+    for _ in range(args.warmup):
+        attn()
+        append()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        attn()
+        ev[i][1].record()
+        append()
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / K
+    att_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    app_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    flops = prefill_flops(w, built.lens_np, w.chunk)
+    tflops = flops / (float(att_ms.mean()) / 1e3) / 1e12
+    result = {
+        "metric": "continuation-prefill chunk tokens/s (attention to compressed history + chunk append)",
+        "value": n / (ms_step / 1e3),
+        "unit": "chunk tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "preset": w.preset,
+                   "head_dim": w.head_dim, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "batch": w.batch, "history": int(built.max_seq_len), "chunk": w.chunk,
+                   "block_size": w.block_size, "parallelism": "single GPU"},
+        "prefill": {"ms_mean": float(att_ms.mean()), "ms_p50": float(np.median(att_ms)), "flops": flops,
+                    "TFLOPs": tflops},
+        "append": {"ms_mean": float(app_ms.mean()), "tokens": n},
+        "roofline": {"bound": "mfma", "kernel": "tq_prefill_attention (layout + split + ring + reduce kernels)",
+                     "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None},
+        "wall_s_timed": wall,
+        "library": tq.version(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = prefill_cpu_baseline(built, cq, ck, cv, args.cpu_budget)
+    print(json.dumps(result))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +376,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w = WORKLOADS[args.workload]
+    if w.chunk:
+        run_prefill(args, w, tq, torch)
+        return
     cfg = tq.config_from_preset(w.preset, w.head_dim) if w.preset else \
         tq.config_init(w.head_dim, w.key_bits, w.value_bits, w.norm_correction, 42)
     from workloads import sequence_lengths

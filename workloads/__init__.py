@@ -18,6 +18,9 @@ Workloads (the five configurations the library is measured and tested on):
               one set to 65536), plus a concurrent 65536-token prefill.
 * ``k3v2_nc`` 3-bit MSE keys + 2-bit values with norm correction (the
               bit-width variant), D=128, 32/8, 64 x 32768 (the 4bit_nc shape).
+* ``prefill_4bit_nc`` continuation prefill: turboquant_4bit_nc, D=128, 32/8,
+              4 sequences with 32768 compressed tokens each and a new
+              512-token chunk each (bf16 q, K, V of the same recipe).
 
 K/V recipe for the D=128 workloads: bf16 N(0,1) with 4 outlier channels per
 KV head scaled x10 (channel sets drawn per head, independently for K and V);
@@ -53,6 +56,7 @@ class Workload:
     seed: int = 0
     block_size: int = 16
     in_dtype: str = "bf16"
+    chunk: int = 0              # continuation-prefill chunk tokens per sequence (prefill workloads)
     description: str = field(default="", compare=False)
 
 
@@ -69,6 +73,9 @@ WORKLOADS = {
     "k3v4_nc": Workload("k3v4_nc", "turboquant_k3v4_nc", 96, 16, 4, 64, 65536, dist="student_t",
                         lognormal_lengths=True, prefill_tokens=65536, seed=1005,
                         description="turboquant_k3v4_nc, D=96, 16q/4kv, 64 log-normal seqs (median 4096, max 65536) + 65536-token prefill"),
+    "prefill_4bit_nc": Workload("prefill_4bit_nc", "turboquant_4bit_nc", 128, 32, 8, 4, 32768, seed=1007, chunk=512,
+                                description="continuation prefill, turboquant_4bit_nc, D=128, 32q/8kv, 4 seqs x "
+                                            "32768 compressed history + 512-token chunk each"),
     "k3v2_nc": Workload("k3v2_nc", None, 128, 32, 8, 64, 32768, key_bits=3, value_bits=2,
                         norm_correction=True, seed=1006,
                         description="3-bit MSE keys + 2-bit values + NC, D=128, 32q/8kv, batch 64, ctx 32768"),
