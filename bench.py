@@ -177,6 +177,50 @@ def ring_flush(built, tq, torch, reps=10):
     return {"tokens": n, "ms": ms, "tokens_per_s": n / (ms / 1e3), "GBps": n * qbpt / (ms / 1e3) / 1e9}
 
 
+def ring_step(built, tq, torch, reps=10):
+    """The device-side ring manager on full rings: tq_ring_flush (every
+    sequence's 128 ring tokens compressed at its next positions, lengths
+    advanced on the device) then tq_ring_append of one new token per sequence.
+    Spare blocks extend each sequence's block table; the lengths and rings are
+    restored between timed reps (outside the events)."""
+    from workloads import KVSource
+    w = built.w
+    bs = w.block_size
+    extra = -(-w.ring // bs)
+    spare = np.asarray(built.spare_blocks, dtype=np.int32)
+    assert len(spare) >= w.batch * extra, "not enough spare blocks"
+    lens = built.lens_np.astype(np.int64)
+    tables = np.zeros((w.batch, int((lens + w.ring + bs - 1).max() // bs)), np.int32)
+    for b in range(w.batch):
+        nb = -(-int(lens[b]) // bs)
+        tables[b, :nb] = built.tables_np[b, :nb]
+        tables[b, nb:nb + extra] = spare[b * extra:(b + 1) * extra]
+    g_tab = torch.from_numpy(tables).cuda()
+    sl0 = built.seq_lens.clone()
+    rl0 = torch.full((w.batch,), w.ring, dtype=torch.int32, device="cuda")
+    rk, rv = built.ring_k.clone(), built.ring_v.clone()
+    sl, rl = sl0.clone(), rl0.clone()
+    kn, vn = KVSource(w, "cuda", stream_id=77).kv(w.batch)
+    kn = kn.reshape(w.batch, w.num_kv_heads, w.head_dim).contiguous()
+    vn = vn.reshape(w.batch, w.num_kv_heads, w.head_dim).contiguous()
+    times = []
+    for i in range(reps + 2):
+        sl.copy_(sl0)
+        rl.copy_(rl0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tq.ring_step(built.cfg, 0, kn, vn, rk, rv, rl, sl, g_tab, built.pools[0])
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1))
+    assert rl.cpu().tolist() == [1] * w.batch and (sl - sl0).cpu().tolist() == [w.ring] * w.batch
+    ms = float(np.mean(times))
+    n = w.batch * w.ring
+    return {"tokens_flushed": n, "ms": ms, "tokens_per_s": n / (ms / 1e3)}
+
+
 def concurrent_prefill(built, tq, torch, steps, reps=10):
     """Decode on the current stream with a prefill quantize-append of
     ``prefill_tokens`` tokens (a sequence outside the batch, written to spare
@@ -430,6 +474,7 @@ def main():
     extra = {}
     if w.ring:
         extra["ring_flush"] = ring_flush(built, tq, torch)
+        extra["ring_step"] = ring_step(built, tq, torch)
     if w.prefill_tokens:
         extra["concurrent_prefill"] = concurrent_prefill(built, tq, torch, steps)
     extra["copy_probe"] = copy = copy_probe(torch)

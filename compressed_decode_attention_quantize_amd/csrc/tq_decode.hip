@@ -90,6 +90,9 @@ struct Geo {
   // one wave's LDS: `bufs` tile buffers, or the queries
   static constexpr int scratch_bytes(int bufs) { return bufs * kTileBuf > kQBytes ? bufs * kTileBuf : kQBytes; }
   static constexpr int kLut = KB == 4 ? 256 : (KB == 3 ? 64 : 1);
+  // every lane's key bytes, and every value code group, start on a word
+  static constexpr bool kKeyAligned = kSlot % 4 == 0 && kLaneKeyBytes % 4 == 0;
+  static constexpr bool kValAligned = kSlot % 4 == 0 && kKeyBytes % 4 == 0 && VB % 4 == 0;
   static_assert(kSlot % 2 == 0, "slot size must be even");
 };
 
@@ -137,10 +140,17 @@ struct Words {
 // NB/4 (rounded up) little-endian words: aligned dword reads and a byte
 // funnel shift. Offsets, not pointer casts, keep the accesses in the LDS
 // address space.
-template <int NB>
+template <int NB, bool kAligned = false>
 __device__ __forceinline__ Words<(NB + 3) / 4> lds_bytes(const uint32_t *words, uint32_t off) {
   constexpr int NW = (NB + 3) / 4;
   const uint32_t w0 = off >> 2;
+  if constexpr (kAligned) {
+    // off is a multiple of 4: whole words, no funnel shift
+    Words<NW> out;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) out.w[i] = words[w0 + i];
+    return out;
+  }
   const uint32_t sh = off & 3u;
   uint32_t raw[NW + 1];
 #pragma unroll
@@ -285,12 +295,12 @@ struct ValueExpand<2> {
 
 // Key operand of one lane: token t = lane % 16, elements kq*D/4 .. +D/4-1 as
 // f16 centroid values (MSE, via the pair table) or FP8-decoded values.
-template <int D, int KB>
+template <int D, int KB, int VB>
 __device__ __forceinline__ void key_operand(const uint32_t *words, uint32_t off, const uint32_t *lut,
                                             half8_t kf[D / 32]) {
-  using G = Geo<D, KB, 4>;
+  using G = Geo<D, KB, VB>;
   constexpr int LB = G::kLaneKeyBytes;
-  const auto kw = lds_bytes<LB>(words, off);
+  const auto kw = lds_bytes<LB, G::kKeyAligned>(words, off);
   if constexpr (KB == 4) {
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) {
@@ -657,7 +667,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         // keys -> scores S^T[4kq + r][col]; this lane keeps them if col is in
         // the tile's column group
         half8_t kf[KM];
-        key_operand<D, KB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
+        key_operand<D, KB, VB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
         float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int m = 0; m < KM; ++m) {
@@ -682,7 +692,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         if constexpr (!kValLds) {
           if (col < GE::kGroups) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vraw[i][r] = lds_bytes<VB>(tw, val_off + r * S).w[0];
+            for (int r = 0; r < 4; ++r) vraw[i][r] = lds_bytes<VB, GE::kValAligned>(tw, val_off + r * S).w[0];
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) vraw[i][r] = 0u;
@@ -752,7 +762,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         const uint32_t *tw = scr + tbuf[i] * (GE::kTileBuf / 4);
         uint32_t vr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? lds_bytes<VB>(tw, val_off + r * S).w[0] : 0u;
+        for (int r = 0; r < 4; ++r)
+          vr[r] = col < GE::kGroups ? lds_bytes<VB, GE::kValAligned>(tw, val_off + r * S).w[0] : 0u;
         VX::prep(vr, pr);  // rows col >= kGroups are padding and never written out
       } else {
         VX::prep(vraw[i], pr);
