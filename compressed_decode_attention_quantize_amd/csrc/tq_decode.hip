@@ -699,8 +699,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
           }
         }
       } else {
-        // tile slot past the end of the segment: all its tokens masked
-        if (lane < 16) tokf[wave][0][i][lane] = -1.0f;
+        // tile slot past the end of the segment: all its tokens masked. The
+        // softmax still multiplies the slot's scale / zero by its zero
+        // weights, so they must be finite: LDS holds whatever an earlier
+        // workgroup left there (packed slot bytes can read as Inf or NaN)
+        if (lane < 16) {
+          tokf[wave][0][i][lane] = -1.0f;
+          tokf[wave][1][i][lane] = 0.0f;
+          tokf[wave][2][i][lane] = 0.0f;
+          tokf[wave][3][i][lane] = 1.0f;
+        }
         tbuf[i] = 0;
       }
     }

@@ -237,6 +237,32 @@ def test_workspace_contents_do_not_matter():
             assert err <= ATTN_RTOL
 
 
+@pytest.mark.parametrize("split", [16, 0])
+def test_repeated_calls_finite_and_identical(split):
+    """Ranges that end inside a macro tile leave tile slots masked; their
+    per-token scale and zero must not come from LDS left over by earlier
+    workgroups (packed slot bytes read as floats can be Inf or NaN, and
+    0 * NaN poisons a row). Ten calls in a row of FP8-key decode with many
+    such ranges: every output finite, within tolerance, and bit-identical."""
+    announce(f"decode repeated calls split={split}")
+    lens = [1777, 900, 3, 0]
+    cfg, ocfg, pool_np, tables, q, ring = _scenario(128, 8, 4, False, 32, 8, lens, seed=44)
+    pool = torch.from_numpy(pool_np).cuda()
+    qd, td, ld = q.cuda(), torch.from_numpy(tables).cuda(), torch.tensor(lens, dtype=torch.int32).cuda()
+    want = OA.decode_attention(q.float().numpy(), pool_np, tables, lens, ocfg, 0)
+    outs = []
+    for _ in range(10):
+        out = tq.decode_attention(cfg, 0, qd, pool, td, ld, max(lens), split_tokens=split)
+        outs.append(out.cpu().numpy())
+    for i, o in enumerate(outs):
+        assert np.isfinite(o).all(), f"call {i}: {int((~np.isfinite(o)).sum())} non-finite outputs"
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), f"call {i} differs"
+    err = per_head_rel_l2(outs[0], want)
+    announce(f"  rel L2 {err:.2e}")
+    assert err <= ATTN_RTOL
+    assert (outs[0][3] == 0).all()
+
+
 def test_empty_context_gives_zeros():
     announce("decode empty")
     cfg = tq.config_from_preset("turboquant_3bit_nc", 128)
