@@ -17,7 +17,8 @@
 //       |c_t|^2   = diag(K~ K~^T)            (norm correction only)
 //       s = S^T * n16_t * scale*log2(e) (/|c_t|), online softmax in exp2,
 //       the running max only ever grows, acc is rescaled when it does
-//       Out^T[j][g] += (code_tj - c0)^T . (p_t s'_t)   MFMA 16x16x16 f16,
+//       Out^T[j][g] += (code_tj - c0)^T . (p_t s'_t)   MFMA 16x16x32 f16
+//                      over tile pairs (K = 2 x 16 tokens),
 //                      codes expanded by the 0x6400 exponent trick in place,
 //                      the weights p_t s'_t as f16 hi + lo parts
 //       zero terms  += p_t (z'_t + c0 s'_t)   fp32
@@ -28,8 +29,7 @@
 //
 // MFMA operand layouts used (gfx950, wave64), checked on hardware:
 //  16x16x32 f16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], e<8;
-//  16x16x16 f16: lane l holds A[l%16][4(l/16)+e], B[4(l/16)+e][l%16], e<4;
-//  both: result lane l register r = D[4(l/16)+r][l%16].
+//  result lane l register r = D[4(l/16)+r][l%16].
 
 #include <algorithm>
 #include <map>
@@ -371,8 +371,11 @@ __device__ __forceinline__ uint32_t lds_u16(const uint32_t *words, uint32_t off)
   return (off & 2u) ? (w >> 16) : (w & 0xffffu);
 }
 
-// NB = tiles per macro tile: the 16 MFMA columns hold NB tile slots of
-// GP = 16 / NB query heads each (NB = 4 for G <= 4, 2 for G <= 8, 1 else).
+// NB = column groups: the 16 MFMA columns hold NB tile slots of GP = 16 / NB
+// query heads each (NB = 4 for G <= 4, 2 for G <= 8, 1 else). A macro tile is
+// NT = NB * TL tiles: with one column group (G > 8) every lane holds the
+// scores of TL = 2 tiles, so that the value contraction still takes two
+// tiles per 16x16x32 MFMA.
 template <int D, int KB, int VB, int NB>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(DecodeParams p, int q_dtype) {
   using GE = Geo<D, KB, VB>;
@@ -380,17 +383,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int S = GE::kSlot;
   constexpr int KM = GE::kKM;
   constexpr int GP = 16 / NB;
-  // Tile buffers per wave. MSE keys with NB > 1 keep all NB tiles of a macro
-  // tile in LDS until the value phase re-reads their codes there (NB + 1
-  // buffers: the next tile loads into the spare one); otherwise two buffers,
-  // the value code words held in registers across the softmax.
-  constexpr bool kValLds = GE::kMse && NB > 1;
-  constexpr int kBufs = kValLds ? NB + 1 : 2;
+  constexpr int TL = NB == 1 ? 2 : 1;  // tiles whose scores one lane holds
+  constexpr int NT = NB * TL;          // tiles per macro tile
+  // Tile buffers per wave. MSE keys keep all NT tiles of a macro tile in LDS
+  // until the value phase re-reads their codes there (NT + 1 buffers: the
+  // next tile loads into the spare one); FP8 keys use two buffers, the value
+  // code words held in registers across the softmax.
+  constexpr bool kValLds = GE::kMse;
+  constexpr int kBufs = kValLds ? NT + 1 : 2;
 
   __shared__ uint32_t lut[GE::kLut];
   __shared__ __align__(16) uint32_t scratch[kWaves][GE::scratch_bytes(kBufs) / 4];
   // per-token scalars of the macro tile: norm * scale (< 0: masked), s', z' + c0 s', ||c||^2
-  __shared__ __align__(16) float tokf[kWaves][4][NB][16];
+  __shared__ __align__(16) float tokf[kWaves][4][NT][16];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -581,12 +586,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   const int end = min(len, static_cast<int>(run_end - seg_start) * kTile);
   f = run_end;
 
-  // ---- macro-tile loop: NB tiles of 16 tokens, tile i in column group i
+  // ---- macro-tile loop: NT tiles of 16 tokens, tile i in column group i % NB
   float4_t acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_lane = 0.0f, z_lane = 0.0f;
-  const int my_tile = col / GP;  // tile slot of this lane's column
+  const int my_tile = col / GP;  // column group of this lane's column
 
   // Tiles go HBM -> LDS by direct loads (global_load_lds_dwordx4: lane l of
   // a load instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS window),
@@ -628,14 +633,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   int bsel = 0;
   // LDS byte offset of element group col's value codes in token 4kq's slot
   const uint32_t val_off = static_cast<uint32_t>(4 * kq * S + GE::kKeyBytes + VB * col);
-  for (int mt0 = begin; mt0 < end; mt0 += NB * kTile) {
-    uint32_t vraw[kValLds ? 1 : NB][4];
-    int tbuf[NB];  // buffer of tile i (wave-uniform)
-    float4_t sraw = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int mt0 = begin; mt0 < end; mt0 += NT * kTile) {
+    uint32_t vraw[kValLds ? 1 : NT][4];
+    int tbuf[NT];  // buffer of tile i (wave-uniform)
+    float4_t sraw[TL];
+#pragma unroll
+    for (int u = 0; u < TL; ++u) sraw[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     // ---- phase A, per tile: scores into the tile's column group, value
     // code words kept in registers, per-token scalars to LDS
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
+    for (int i = 0; i < NT; ++i) {
       const int tile0 = mt0 + i * kTile;
       if (tile0 < end) {
         const int ntok = min(kTile, end - tile0);
@@ -674,7 +681,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
           sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[m], sc, 0, 0, 0);
           sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], ql[m], sc, 0, 0, 0);
         }
-        if (my_tile == i) sraw = sc;
+        if constexpr (TL == 1) {
+          if (my_tile == i) sraw[0] = sc;
+        } else {
+          sraw[i] = sc;
+        }
         if constexpr (GE::kMse) {
           if (nc) {
             // ||c_t||^2 of token t = 4kq + r sits on the Gram diagonal, at
@@ -714,26 +725,32 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     }
 
     // ---- phase B, once per macro tile: lane (kq, col) holds tokens
-    // 4kq..4kq+3 of tile my_tile for query head col % GP
+    // 4kq..4kq+3 of tile my_tile (TL = 1) or of both tiles (TL = 2) for query
+    // head col % GP
     wave_lds_sync();  // per-token scalars written by other lanes
-    const float4_t fb4 = *reinterpret_cast<const float4_t *>(&tokf[wave][0][my_tile][4 * kq]);
-    const float4_t s14 = *reinterpret_cast<const float4_t *>(&tokf[wave][1][my_tile][4 * kq]);
-    const float4_t zc4 = *reinterpret_cast<const float4_t *>(&tokf[wave][2][my_tile][4 * kq]);
-    float4_t nn4 = {1.0f, 1.0f, 1.0f, 1.0f};
-    if (nc) nn4 = *reinterpret_cast<const float4_t *>(&tokf[wave][3][my_tile][4 * kq]);
-    float s[4];
+    float s[TL][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float f = fb4[r];
-      if constexpr (GE::kMse) {
-        // centroids carry the table scale sigma: it cancels under norm
-        // correction and is divided out otherwise
-        f *= nc ? __builtin_amdgcn_rsqf(nn4[r]) : inv_sigma;
+    for (int u = 0; u < TL; ++u) {
+      const int ti = TL == 1 ? my_tile : u;
+      const float4_t fb4 = *reinterpret_cast<const float4_t *>(&tokf[wave][0][ti][4 * kq]);
+      float4_t nn4 = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (nc) nn4 = *reinterpret_cast<const float4_t *>(&tokf[wave][3][ti][4 * kq]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float f = fb4[r];
+        if constexpr (GE::kMse) {
+          // centroids carry the table scale sigma: it cancels under norm
+          // correction and is divided out otherwise
+          f *= nc ? __builtin_amdgcn_rsqf(nn4[r]) : inv_sigma;
+        }
+        s[u][r] = (fb4[r] >= 0.0f) ? sraw[u][r] * f : -INFINITY;
       }
-      s[r] = (fb4[r] >= 0.0f) ? sraw[r] * f : -INFINITY;
     }
-    // running max of the column: 4 registers, then the 4 lane rows
-    const float mt = column_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    // running max of the column: the lane's registers, then the 4 lane rows
+    float mloc = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+    for (int u = 1; u < TL; ++u) mloc = fmaxf(mloc, fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3])));
+    const float mt = column_max(mloc);
     if (mt > m_run) {
       const float alpha = exp2f(m_run - mt);
 #pragma unroll
@@ -743,26 +760,34 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       m_run = mt;
     }
     const float mr = (m_run == -INFINITY) ? 0.0f : m_run;
-    float w[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float pr = __builtin_amdgcn_exp2f(s[r] - mr);
-      l_lane += pr;
-      z_lane = fmaf(pr, zc4[r], z_lane);
-      w[r] = pr * s14[r];
-    }
     // weights p * s' as f16 hi + lo parts: the value contraction then sees
     // them to ~22 bits (f16 alone leaves a 2^-12 error that cancellation in
     // the weighted sum can amplify)
-    u32x2_t hw, lw;
-    hw[0] = f16_pair_bits(w[0], w[1]);
-    hw[1] = f16_pair_bits(w[2], w[3]);
-    lw[0] = f16_pair_bits(w[0] - f16_bits_to_float(hw[0] & 0xffffu), w[1] - f16_bits_to_float(hw[0] >> 16));
-    lw[1] = f16_pair_bits(w[2] - f16_bits_to_float(hw[1] & 0xffffu), w[3] - f16_bits_to_float(hw[1] >> 16));
+    u32x2_t hw[TL], lw[TL];
+#pragma unroll
+    for (int u = 0; u < TL; ++u) {
+      const int ti = TL == 1 ? my_tile : u;
+      const float4_t s14 = *reinterpret_cast<const float4_t *>(&tokf[wave][1][ti][4 * kq]);
+      const float4_t zc4 = *reinterpret_cast<const float4_t *>(&tokf[wave][2][ti][4 * kq]);
+      float w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(s[u][r] - mr);
+        l_lane += pr;
+        z_lane = fmaf(pr, zc4[r], z_lane);
+        w[r] = pr * s14[r];
+      }
+      hw[u][0] = f16_pair_bits(w[0], w[1]);
+      hw[u][1] = f16_pair_bits(w[2], w[3]);
+      lw[u][0] = f16_pair_bits(w[0] - f16_bits_to_float(hw[u][0] & 0xffffu),
+                               w[1] - f16_bits_to_float(hw[u][0] >> 16));
+      lw[u][1] = f16_pair_bits(w[2] - f16_bits_to_float(hw[u][1] & 0xffffu),
+                               w[3] - f16_bits_to_float(hw[u][1] >> 16));
+    }
     wave_lds_sync();  // scalar reads done before the next macro tile rewrites them
 
-    // ---- phase C, per tile: value MFMAs with the weights of the tile's
-    // column group only (zero elsewhere)
+    // ---- phase C: value MFMAs, the weights of each tile in its own column
+    // group only (zero elsewhere)
     // value code bytes of tile i for this lane's element group, gathered
     auto prep_tile = [&](int i, typename VX::Prep &pr) {
       if constexpr (kValLds) {
@@ -777,60 +802,48 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         VX::prep(vraw[i], pr);
       }
     };
-    if constexpr (NB >= 2) {
-      // Tiles in pairs: one 16x16x32 MFMA takes tokens 4kq..4kq+3 of tile i
-      // in K slots 8kq..8kq+3 and those of tile i+1 in 8kq+4..8kq+7, with
-      // each tile's weights masked to its own column group.
+    // Tiles in pairs: one 16x16x32 MFMA takes tokens 4kq..4kq+3 of tile i in
+    // K slots 8kq..8kq+3 and those of tile i+1 in 8kq+4..8kq+7, each tile's
+    // weights masked to its own column group (TL = 1) or both unmasked
+    // (TL = 2: every column is in both tiles' group).
 #pragma unroll
-      for (int i = 0; i < NB; i += 2) {
-        if (mt0 + i * kTile < end) {
-          const bool has1 = mt0 + (i + 1) * kTile < end;
+    for (int i = 0; i < NT; i += 2) {
+      if (mt0 + i * kTile < end) {
+        const bool has1 = mt0 + (i + 1) * kTile < end;
+        u32x4_t bh, bl;
+        if constexpr (TL == 1) {
           const bool m0 = my_tile == i, m1 = my_tile == i + 1;
-          u32x4_t bh, bl;
-          bh[0] = m0 ? hw[0] : 0u;
-          bh[1] = m0 ? hw[1] : 0u;
-          bh[2] = m1 ? hw[0] : 0u;
-          bh[3] = m1 ? hw[1] : 0u;
-          bl[0] = m0 ? lw[0] : 0u;
-          bl[1] = m0 ? lw[1] : 0u;
-          bl[2] = m1 ? lw[0] : 0u;
-          bl[3] = m1 ? lw[1] : 0u;
-          const half8_t pvh = __builtin_bit_cast(half8_t, bh);
-          const half8_t pvl = __builtin_bit_cast(half8_t, bl);
-          typename VX::Prep p0, p1;
-          prep_tile(i, p0);
-          // past the end of the range the second half's weights are zero
-          // (masked tokens), so any finite codes do: reuse the first tile's
-          if (has1) prep_tile(i + 1, p1);
-          else p1 = p0;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const half8_t av = __builtin_shufflevector(VX::get(p0, c), VX::get(p1, c), 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pvh, acc[c], 0, 0, 0);
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pvl, acc[c], 0, 0, 0);
-          }
+          bh[0] = m0 ? hw[0][0] : 0u;
+          bh[1] = m0 ? hw[0][1] : 0u;
+          bh[2] = m1 ? hw[0][0] : 0u;
+          bh[3] = m1 ? hw[0][1] : 0u;
+          bl[0] = m0 ? lw[0][0] : 0u;
+          bl[1] = m0 ? lw[0][1] : 0u;
+          bl[2] = m1 ? lw[0][0] : 0u;
+          bl[3] = m1 ? lw[0][1] : 0u;
+        } else {
+          bh[0] = hw[0][0];
+          bh[1] = hw[0][1];
+          bh[2] = hw[1][0];
+          bh[3] = hw[1][1];
+          bl[0] = lw[0][0];
+          bl[1] = lw[0][1];
+          bl[2] = lw[1][0];
+          bl[3] = lw[1][1];
         }
-      }
-    } else {
+        const half8_t pvh = __builtin_bit_cast(half8_t, bh);
+        const half8_t pvl = __builtin_bit_cast(half8_t, bl);
+        typename VX::Prep p0, p1;
+        prep_tile(i, p0);
+        // past the end of the range the second half's weights are zero
+        // (masked tokens), so any finite codes do: reuse the first tile's
+        if (has1) prep_tile(i + 1, p1);
+        else p1 = p0;
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        if (mt0 + i * kTile < end) {
-          const bool mine = my_tile == i;
-          u32x2_t bh, bl;
-          bh[0] = mine ? hw[0] : 0u;
-          bh[1] = mine ? hw[1] : 0u;
-          bl[0] = mine ? lw[0] : 0u;
-          bl[1] = mine ? lw[1] : 0u;
-          const half4_t pvh = __builtin_bit_cast(half4_t, bh);
-          const half4_t pvl = __builtin_bit_cast(half4_t, bl);
-          typename VX::Prep p0;
-          prep_tile(i, p0);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const half4_t av = VX::get(p0, c);
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pvh, acc[c], 0, 0, 0);
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pvl, acc[c], 0, 0, 0);
-          }
+        for (int c = 0; c < 8; ++c) {
+          const half8_t av = __builtin_shufflevector(VX::get(p0, c), VX::get(p1, c), 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pvh, acc[c], 0, 0, 0);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pvl, acc[c], 0, 0, 0);
         }
       }
     }
