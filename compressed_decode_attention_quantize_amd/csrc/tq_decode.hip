@@ -365,6 +365,19 @@ __device__ __forceinline__ float column_sum(float v) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// Value of the lane N columns away in the lane's 16-lane row (DPP row_ror:N:
+// lane c reads lane (c - N) mod 16 of its row; for N = 8 that is the partner
+// half of the row either way).
+template <int N>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
+  static_assert(N > 0 && N < 16, "row rotation");
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x120 + N, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __uint_as_float(row_ror<N>(__float_as_uint(v)));
+}
+
 // 16-bit field at an even byte offset of an LDS word array.
 __device__ __forceinline__ uint32_t lds_u16(const uint32_t *words, uint32_t off) {
   const uint32_t w = words[off >> 2];
@@ -376,6 +389,16 @@ __device__ __forceinline__ uint32_t lds_u16(const uint32_t *words, uint32_t off)
 // NT = NB * TL tiles: with one column group (G > 8) every lane holds the
 // scores of TL = 2 tiles, so that the value contraction still takes two
 // tiles per 16x16x32 MFMA.
+//
+// With NB > 1 the f16 hi and lo parts of an operand share one MFMA: group j
+// and its partner j +- NB/2 (the lanes 8 columns away, same row) carry the
+// two parts of the same query heads, and one DPP row rotation adds them.
+//  scores: tile i (kept by group i) multiplies the plane with the hi parts
+//          in group i and the lo parts in its partner;
+//  values: the weights of tile i go to group i as hi parts and to the
+//          partner group as lo parts, so every group accumulates a mix of
+//          tiles. All groups of a query head therefore share one running
+//          maximum, and the final merge of the groups is a plain sum.
 template <int D, int KB, int VB, int NB>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(DecodeParams p, int q_dtype) {
   using GE = Geo<D, KB, VB>;
@@ -385,6 +408,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int GP = 16 / NB;
   constexpr int TL = NB == 1 ? 2 : 1;  // tiles whose scores one lane holds
   constexpr int NT = NB * TL;          // tiles per macro tile
+  constexpr bool kFold = NB > 1;       // hi and lo parts in partner column groups
   // Tile buffers per wave. MSE keys keep all NT tiles of a macro tile in LDS
   // until the value phase re-reads their codes there (NT + 1 buffers: the
   // next tile loads into the spare one); FP8 keys use two buffers, the value
@@ -558,7 +582,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       qhi[k] = hv;
       qlo[k] = lv;
     }
-    // hi parts through LDS into the MFMA operand layout, then the lo parts
+    // hi parts through LDS into the MFMA operand layout, then the lo parts.
+    // With partner groups (kFold) the first plane (qf) has the hi parts in
+    // groups < NB/2 and the lo parts in the others, the second (ql) the
+    // opposite.
     _Float16 *qs = reinterpret_cast<_Float16 *>(scr);
 #pragma unroll
     for (int phase = 0; phase < 2; ++phase) {
@@ -568,8 +595,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         const int g = k * rows_per_pass + team;
         if (team < rows_per_pass && g < GP) {
 #pragma unroll
-          for (int j = 0; j < NB; ++j)
-            *reinterpret_cast<u32x4_t *>(qs + (j * GP + g) * D + 8 * r) = phase == 0 ? qhi[k] : qlo[k];
+          for (int j = 0; j < NB; ++j) {
+            const bool hi_part = kFold ? ((phase == 0) == (j < NB / 2)) : (phase == 0);
+            *reinterpret_cast<u32x4_t *>(qs + (j * GP + g) * D + 8 * r) = hi_part ? qhi[k] : qlo[k];
+          }
         }
       }
       wave_lds_sync();  // the rows other lanes wrote are visible
@@ -676,10 +705,20 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         half8_t kf[KM];
         key_operand<D, KB, VB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
         float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (kFold) {
+          // hi parts in group i, lo parts in its partner: one MFMA per K
+          // step, then the partner's column is added
 #pragma unroll
-        for (int m = 0; m < KM; ++m) {
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[m], sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], ql[m], sc, 0, 0, 0);
+          for (int m = 0; m < KM; ++m)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], i < NB / 2 ? qf[m] : ql[m], sc, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[r] += row_ror<8>(sc[r]);
+        } else {
+#pragma unroll
+          for (int m = 0; m < KM; ++m) {
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[m], sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], ql[m], sc, 0, 0, 0);
+          }
         }
         if constexpr (TL == 1) {
           if (my_tile == i) sraw[0] = sc;
@@ -750,7 +789,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     float mloc = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
 #pragma unroll
     for (int u = 1; u < TL; ++u) mloc = fmaxf(mloc, fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3])));
-    const float mt = column_max(mloc);
+    float mt = column_max(mloc);
+    if constexpr (kFold) {
+      // one maximum per query head over all column groups
+      if constexpr (NB == 4) mt = fmaxf(mt, row_ror<4>(mt));
+      mt = fmaxf(mt, row_ror<8>(mt));
+    }
     if (mt > m_run) {
       const float alpha = exp2f(m_run - mt);
 #pragma unroll
@@ -806,10 +850,40 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     // K slots 8kq..8kq+3 and those of tile i+1 in 8kq+4..8kq+7, each tile's
     // weights masked to its own column group (TL = 1) or both unmasked
     // (TL = 2: every column is in both tiles' group).
+    // With partner groups the lo weights of tile t reach group t's partner
+    // (the lanes 8 columns away, which hold another tile's scores).
+    uint32_t lx[2] = {0u, 0u};
+    if constexpr (kFold) {
+      lx[0] = row_ror<8>(lw[0][0]);
+      lx[1] = row_ror<8>(lw[0][1]);
+    }
 #pragma unroll
     for (int i = 0; i < NT; i += 2) {
       if (mt0 + i * kTile < end) {
         const bool has1 = mt0 + (i + 1) * kTile < end;
+        if constexpr (kFold) {
+          // K rows of tile t: hi weights in group t, lo weights in group
+          // (t + NB/2) mod NB, zero elsewhere
+          auto pick = [&](int t, int e) -> uint32_t {
+            return my_tile == t ? hw[0][e] : (my_tile == (t + NB / 2) % NB ? lx[e] : 0u);
+          };
+          u32x4_t bw;
+          bw[0] = pick(i, 0);
+          bw[1] = pick(i, 1);
+          bw[2] = pick(i + 1, 0);
+          bw[3] = pick(i + 1, 1);
+          const half8_t pv = __builtin_bit_cast(half8_t, bw);
+          typename VX::Prep p0, p1;
+          prep_tile(i, p0);
+          if (has1) prep_tile(i + 1, p1);
+          else p1 = p0;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const half8_t av = __builtin_shufflevector(VX::get(p0, c), VX::get(p1, c), 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pv, acc[c], 0, 0, 0);
+          }
+          continue;
+        }
         u32x4_t bh, bl;
         if constexpr (TL == 1) {
           const bool m0 = my_tile == i, m1 = my_tile == i + 1;
