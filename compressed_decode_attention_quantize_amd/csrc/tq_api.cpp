@@ -203,6 +203,8 @@ TQ_EXPORT tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx, co
     return fail(TQ_ERR_INVALID_ARG, "tq_prefill_attention: invalid sizes (num_q_heads must be a multiple of num_kv_heads)");
   if (block_size <= 0 || block_size % 16 != 0)
     return fail(TQ_ERR_UNSUPPORTED, "tq_prefill_attention: block_size must be a positive multiple of 16");
+  if (static_cast<int64_t>(num_kv_heads) * block_size * cfg->slot_size_aligned > INT32_MAX)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_prefill_attention: a pool block (num_kv_heads * block_size * slot bytes) must be below 2 GiB");
   if (!valid_dtype(q_dtype)) return fail(TQ_ERR_INVALID_ARG, "tq_prefill_attention: unknown q dtype");
   if (batch == 0 || max_chunk == 0) return TQ_OK;
   if (!q || !k_chunk || !v_chunk || !cu_chunk || !kv_pool || !block_tables || !hist_lens || !out)
@@ -336,6 +338,8 @@ TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, con
     return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: at most 16 query heads per KV head");
   if (block_size <= 0 || block_size % 16 != 0)
     return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: block_size must be a positive multiple of 16");
+  if (static_cast<int64_t>(num_kv_heads) * block_size * cfg->slot_size_aligned > INT32_MAX)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: a pool block (num_kv_heads * block_size * slot bytes) must be below 2 GiB");
   if (max_seq_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0 || ring_cap < 0)
     return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: negative size argument");
   if (!valid_dtype(q_dtype)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: unknown q dtype");

@@ -418,8 +418,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
 
   __shared__ uint32_t lut[GE::kLut];
   __shared__ __align__(16) uint32_t scratch[kWaves][GE::scratch_bytes(kBufs) / 4];
-  // per-token scalars of the macro tile: norm * scale (< 0: masked), s', z' + c0 s', ||c||^2
-  __shared__ __align__(16) float tokf[kWaves][4][NT][16];
+  // per-token scalars of the macro tile: norm * scale (< 0: masked), s', z' + c0 s', ||c||^2;
+  // plane 4 takes the writes of lanes that hold nothing for a plane
+  __shared__ __align__(16) float tokf[kWaves][5][NT][16];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -505,10 +506,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   // its first 64 blocks (lane i: logical block blk_base + i) and, below, the
   // query rows.
   const int len_raw = p.seq_lens[b];
-  int blk_base = begin / p.block_size;
-  int blk_lane = blk_base + lane < p.max_blocks_per_seq
-                     ? p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + blk_base + lane]
-                     : 0;
+  const int32_t *bt_row = p.block_tables + static_cast<int64_t>(b) * p.max_blocks_per_seq;
+  // the next tile to load: logical block and first token in it, advanced by
+  // one tile per load (tiles of a range are loaded in order)
+  int nx_blk = begin / p.block_size;
+  int nx_off = begin - nx_blk * p.block_size;
+  int blk_base = nx_blk;
+  int blk_lane = blk_base + lane < p.max_blocks_per_seq ? bt_row[blk_base + lane] : 0;
   float *part_base = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + h * G) * p.splits_total * pstride +
                      static_cast<int64_t>(slot) * pstride;
 
@@ -629,23 +633,31 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   // Block ids of the range, 64 at a time (blk_base, blk_lane above); tiles
   // pick theirs with readlane.
   bool ok_next = false;
-  auto issue = [&](int tile0, int bsel) {
-    const int lblk = tile0 / p.block_size;
-    const int off = tile0 - lblk * p.block_size;
+  // bytes of one pool block (all heads; the host keeps it below 2^31) and
+  // this head's run inside a block
+  const uint32_t blk_stride = static_cast<uint32_t>(p.num_kv_heads * p.block_size * S);
+  const uint8_t *head_base = p.pool + static_cast<int64_t>(h) * p.block_size * S;
+  const uint32_t nblk = static_cast<uint32_t>(p.num_blocks < 0x7fffffff ? p.num_blocks : 0x7fffffff);
+  auto issue = [&](int bsel) {
+    const int rel = nx_blk - blk_base;
     int phys;
-    if (lblk - blk_base >= 64) {
+    if (rel >= 64) {
       // refill the window; the wait for this load stays on this branch
-      blk_base = lblk;
-      const int bi = blk_base + lane;
-      blk_lane = bi < p.max_blocks_per_seq ? p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + bi] : 0;
+      blk_base = nx_blk;
+      blk_lane = blk_base + lane < p.max_blocks_per_seq ? bt_row[blk_base + lane] : 0;
       phys = __builtin_amdgcn_readlane(blk_lane, 0);
     } else {
-      phys = __builtin_amdgcn_readlane(blk_lane, lblk - blk_base);
+      phys = __builtin_amdgcn_readlane(blk_lane, rel);
     }
-    ok_next = phys >= 0 && phys < p.num_blocks;
-    // an invalid block reads the pool's first tile instead (its tokens are masked)
-    const uint8_t *src = p.pool + ((static_cast<int64_t>(ok_next ? phys : 0) * p.num_kv_heads + h) * p.block_size + off) *
-                                      static_cast<int64_t>(S);
+    ok_next = static_cast<uint32_t>(phys) < nblk;
+    // an invalid block reads the pool's first block instead (its tokens are masked)
+    const uint8_t *src = head_base + static_cast<uint64_t>(ok_next ? static_cast<uint32_t>(phys) : 0u) * blk_stride +
+                         static_cast<uint32_t>(nx_off * S);
+    nx_off += kTile;
+    if (nx_off == p.block_size) {
+      nx_off = 0;
+      ++nx_blk;
+    }
     const uint32_t dst = lds_offset(scratch[wave]) + bsel * GE::kTileBuf;
     wait_lds_reads();  // earlier reads of this buffer (or the query plane) have executed
 #pragma unroll
@@ -654,7 +666,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       if (c < GE::kTileChunks) load_lds_16(src + 16 * c, dst + 1024 * k);
     }
   };
-  issue(begin, 0);  // waits for the query plane reads before overwriting it
+  issue(0);  // waits for the query plane reads before overwriting it
 
   const float c0 = static_cast<float>(VX::kC0);
   const float inv_sigma = 1.0f / p.centroid_scale;
@@ -678,7 +690,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         const bool tile_ok = ok_next;
         const int nsel = bsel + 1 == kBufs ? 0 : bsel + 1;
         if (tile0 + kTile < end) {
-          issue(tile0 + kTile, nsel);
+          issue(nsel);
           wait_vmcnt<kLoads>();  // this tile's loads are done, the next tile's may run
         } else {
           wait_vmcnt<0>();
@@ -687,17 +699,20 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         tbuf[i] = bsel;
         bsel = nsel;
 
-        // per-token scalars: lane t < 16 reads its slot's norm / scale / zero
-        if (lane < 16) {
-          const uint32_t slot = static_cast<uint32_t>(lane * S);
-          const bool ok = tile_ok && lane < ntok;
-          float fb = p.scale_log2;
-          if constexpr (GE::kMse) fb *= f16_bits_to_float(lds_u16(tw, slot + GE::kKeyCodeBytes));
-          const float s1 = f16_bits_to_float(lds_u16(tw, slot + GE::kKeyBytes + GE::kValCodeBytes));
-          const float z1 = f16_bits_to_float(lds_u16(tw, slot + GE::kKeyBytes + GE::kValCodeBytes + 2));
-          tokf[wave][0][i][lane] = ok ? fb : -1.0f;  // negative marks a masked token
-          tokf[wave][1][i][lane] = ok ? s1 : 0.0f;
-          tokf[wave][2][i][lane] = ok ? fmaf(c0, s1, z1) : 0.0f;
+        // per-token scalars of token col, plane kq: the norm times the
+        // softmax scale (negative marks a masked token), s', z' + c0 s', and
+        // 1 in plane 3 (the norm-correction pass overwrites it)
+        {
+          const uint32_t slot = static_cast<uint32_t>(col * S);
+          constexpr uint32_t kScaleOff = GE::kKeyBytes + GE::kValCodeBytes;
+          const float a = f16_bits_to_float(lds_u16(tw, slot + (kq == 0 ? GE::kKeyCodeBytes : kScaleOff)));
+          const float z1 = f16_bits_to_float(lds_u16(tw, slot + kScaleOff + 2));
+          const bool ok = tile_ok && col < ntok;
+          const float fb = GE::kMse ? p.scale_log2 * a : p.scale_log2;
+          float val = kq == 0 ? (ok ? fb : -1.0f) : (kq == 1 ? a : fmaf(c0, a, z1));
+          if (kq != 0 && !ok) val = 0.0f;
+          if (kq == 3) val = 1.0f;
+          tokf[wave][kq][i][col] = val;
         }
 
         // keys -> scores S^T[4kq + r][col]; this lane keeps them if col is in
@@ -734,7 +749,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
             for (int m = 0; m < KM; ++m) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], kf[m], gram, 0, 0, 0);
             const int rr = col - 4 * kq;
             const float dg = rr == 0 ? gram[0] : rr == 1 ? gram[1] : rr == 2 ? gram[2] : gram[3];
-            if (rr >= 0 && rr < 4) tokf[wave][3][i][col] = dg;
+            tokf[wave][rr >= 0 && rr < 4 ? 3 : 4][i][col] = dg;
           }
         }
 
@@ -753,12 +768,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         // softmax still multiplies the slot's scale / zero by its zero
         // weights, so they must be finite: LDS holds whatever an earlier
         // workgroup left there (packed slot bytes can read as Inf or NaN)
-        if (lane < 16) {
-          tokf[wave][0][i][lane] = -1.0f;
-          tokf[wave][1][i][lane] = 0.0f;
-          tokf[wave][2][i][lane] = 0.0f;
-          tokf[wave][3][i][lane] = 1.0f;
-        }
+        tokf[wave][kq][i][col] = kq == 0 ? -1.0f : (kq == 3 ? 1.0f : 0.0f);
         tbuf[i] = 0;
       }
     }

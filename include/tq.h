@@ -322,7 +322,9 @@ tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, int num_q_he
  *  out           device fp32 [batch][num_q_heads][head_dim], 16-byte aligned.
  *  workspace     device, at least tq_decode_workspace_size bytes, 16-byte
  *                aligned; its contents on entry do not matter.
- *  block_size    a multiple of 16.
+ *  block_size    a multiple of 16; one pool block (num_kv_heads * block_size
+ *                * slot_size_aligned bytes) below 2 GiB (TQ_ERR_UNSUPPORTED
+ *                otherwise).
  */
 tq_status tq_decode_attention(const tq_config *cfg, int layer_idx,
                               const void *q, tq_dtype q_dtype,
