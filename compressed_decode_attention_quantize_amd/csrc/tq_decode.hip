@@ -983,10 +983,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
 }
 
 // Exact bf16 ring tokens: fp32 VALU, one workgroup per (sequence, KV head,
-// 64-token chunk of the ring), writing partial slot max_splits + chunk of the
-// sequence's query heads. K rows and V transposed go through LDS; scores
-// (thread = token x head group), softmax of the chunk (wave = head, lane =
-// token), then P.V (thread = output column x head group).
+// kRingChunk-token chunk of the ring), writing partial slot max_splits + chunk
+// of the sequence's query heads. The query rows and the chunk's K/V rows are
+// all loaded before any of them is stored (one round trip to memory); K rows
+// and V transposed go through LDS; scores (thread = token x head group),
+// softmax of the chunk (wave = head, lane = token), then P.V (thread = output
+// column x head group).
 constexpr int kRingThreads = 256;
 constexpr int kMaxG = 16;
 
@@ -1003,13 +1005,16 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 template <int D>
 __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams p, int q_dtype) {
+  static_assert(kRingChunk <= 64 && kRingChunk % 8 == 0, "a chunk's softmax runs on one wave");
   constexpr int kRow = D + 8;                       // bf16 per K row in LDS (16 bytes of padding)
   constexpr int kTRow = kRingChunk + 8;             // bf16 per transposed V row
   constexpr int kVec = D / 8;                       // 16-byte vectors per K/V row
   constexpr int kHeadGroups = kRingThreads / D;     // P.V: threads per output column
   constexpr int kAcc = (kMaxG + kHeadGroups - 1) / kHeadGroups;
   constexpr int kScoreGroups = kRingThreads / kRingChunk;
-  constexpr int kScoreHeads = kMaxG / kScoreGroups;
+  constexpr int kScoreHeads = (kMaxG + kScoreGroups - 1) / kScoreGroups;
+  constexpr int kKvLoads = (kRingChunk * kVec + kRingThreads - 1) / kRingThreads;
+  constexpr int kQLoads = (kMaxG * D + kRingThreads - 1) / kRingThreads;
   __shared__ float q_s[kMaxG][D];
   __shared__ __align__(16) uint16_t k_s[kRingChunk][kRow];
   __shared__ __align__(16) uint16_t vt_s[D][kTRow];
@@ -1028,24 +1033,42 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
   const int64_t part0 = static_cast<int64_t>(b) * p.num_q_heads + h * G;
   const int slot = p.max_splits + chunk;
 
-  for (int e = tid; e < G * D; e += kRingThreads) {
-    const int g = e / D, j = e - (e / D) * D;
-    q_s[g][j] = load_as_float(p.q, q_dtype, (static_cast<int64_t>(b) * p.num_q_heads + h * G + g) * D + j);
-  }
   const int rb = p.ring_group > 0 ? b / p.ring_group : b;  // the ring this sequence reads
   const int64_t ring0 = ((static_cast<int64_t>(rb) * p.num_kv_heads + h) * p.ring_cap + c0) * D;
-  for (int e = tid; e < kRingChunk * kVec; e += kRingThreads) {
-    const int t = e % kRingChunk, c = e / kRingChunk;
-    u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (t < n) {
-      kv = *reinterpret_cast<const u32x4_t *>(p.ring_k + ring0 + t * D + 8 * c);
-      vv = *reinterpret_cast<const u32x4_t *>(p.ring_v + ring0 + t * D + 8 * c);
-    }
-    *reinterpret_cast<u32x4_t *>(&k_s[t][8 * c]) = kv;
+  float qv[kQLoads];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vt_s[8 * c + 2 * i][t] = static_cast<uint16_t>(vv[i] & 0xffffu);
-      vt_s[8 * c + 2 * i + 1][t] = static_cast<uint16_t>(vv[i] >> 16);
+  for (int i = 0; i < kQLoads; ++i) {
+    const int e = tid + i * kRingThreads;
+    qv[i] = e < G * D ? load_as_float(p.q, q_dtype, part0 * D + e) : 0.0f;
+  }
+  u32x4_t kv[kKvLoads], vv[kKvLoads];
+#pragma unroll
+  for (int i = 0; i < kKvLoads; ++i) {
+    const int e = tid + i * kRingThreads;
+    const int t = e % kRingChunk, c = e / kRingChunk;
+    kv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    vv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (c < kVec && t < n) {
+      kv[i] = *reinterpret_cast<const u32x4_t *>(p.ring_k + ring0 + t * D + 8 * c);
+      vv[i] = *reinterpret_cast<const u32x4_t *>(p.ring_v + ring0 + t * D + 8 * c);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kQLoads; ++i) {
+    const int e = tid + i * kRingThreads;
+    if (e < G * D) q_s[e / D][e % D] = qv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kKvLoads; ++i) {
+    const int e = tid + i * kRingThreads;
+    const int t = e % kRingChunk, c = e / kRingChunk;
+    if (c < kVec) {
+      *reinterpret_cast<u32x4_t *>(&k_s[t][8 * c]) = kv[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vt_s[8 * c + 2 * j][t] = static_cast<uint16_t>(vv[i][j] & 0xffffu);
+        vt_s[8 * c + 2 * j + 1][t] = static_cast<uint16_t>(vv[i][j] >> 16);
+      }
     }
   }
   __syncthreads();
@@ -1089,20 +1112,17 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kScoreHeads; ++i) {
-    const int g = wave + kScoreGroups * i;  // one wave per head, lane = token
-    if (g < G) {
-      const float sc = p_s[g][lane];
-      const float m = wave_max(sc);
-      const float pt = (sc == -INFINITY) ? 0.0f : exp2f(sc - m);
-      p_s[g][lane] = pt;
-      const float l = wave_sum(pt);
-      if (lane == 0) {
-        float *dst = p.partials + ((part0 + g) * p.splits_total + slot) * pstride;
-        dst[0] = m;
-        dst[1] = l;
-      }
+  for (int g = wave; g < G; g += kRingThreads / 64) {
+    // one wave per head, lane = token (lanes past the chunk hold nothing)
+    const float sc = lane < kRingChunk ? p_s[g][lane] : -INFINITY;
+    const float m = wave_max(sc);
+    const float pt = (sc == -INFINITY) ? 0.0f : exp2f(sc - m);
+    if (lane < kRingChunk) p_s[g][lane] = pt;
+    const float l = wave_sum(pt);
+    if (lane == 0) {
+      float *dst = p.partials + ((part0 + g) * p.splits_total + slot) * pstride;
+      dst[0] = m;
+      dst[1] = l;
     }
   }
   __syncthreads();

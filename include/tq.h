@@ -286,8 +286,8 @@ tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx,
  * is balanced whatever the mix of lengths. The workspace holds a header
  * (16 + 4 (batch + 1) bytes, rounded up to 256) and one fp32 partial
  * (max, sum, acc[head_dim]) per (sequence, query head, slot) with
- * ceil(max_seq_len / min tokens) + 1 slots, plus one per 64 ring tokens
- * (ceil(ring_cap / 64)). num_splits_out (nullable) receives the slots per
+ * ceil(max_seq_len / min tokens) + 1 slots, plus one per 32 ring tokens
+ * (ceil(ring_cap / 32)). num_splits_out (nullable) receives the slots per
  * sequence.
  */
 tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, int num_q_heads,

@@ -185,11 +185,11 @@ def test_workspace_size_and_plan():
     # a wave covers >= 256 tokens, so a sequence spans <= 8192/256 + 1 waves
     b, n = tq.decode_workspace_size(c, 16, 32, 8192, 0, 256)
     assert n == 33 and b == 256 + 16 * 32 * 33 * 132 * 4
-    # one partial slot per 64 ring tokens
+    # one partial slot per 32 ring tokens
     b, n = tq.decode_workspace_size(c, 16, 32, 8192, 128, 256)
-    assert n == 35
+    assert n == 37
     _, n = tq.decode_workspace_size(c, 16, 32, 8192, 100, 256)
-    assert n == 35
+    assert n == 37
     b, n = tq.decode_workspace_size(c, 4, 8, 0, 0, 0)
     assert n == 0 and b == 256 + 4 * 8 * 1 * 132 * 4
     _, n_auto = tq.decode_workspace_size(c, 16, 32, 8192)
