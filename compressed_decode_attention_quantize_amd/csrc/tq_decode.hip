@@ -180,13 +180,19 @@ __device__ __forceinline__ uint32_t f16_pair_bits(float lo, float hi) {
 // `mask` selects the element's field in place (bits <= 9), so
 // (x & mask) | 0x6400 is the f16 1024 + code * 2^pos in each half; adding
 // -(1024 + 2^pos * c0) leaves 2^pos * (code - c0), exact in f16.
+//
+// The mask and the exponent constant reach the compiler as register values it
+// cannot see into (empty asm with a register constraint), so it selects one
+// v_and_or_b32 with register operands: gfx950 VOP3 encodings take no literal,
+// and with literals it would split the expression into v_and + v_or.
+__device__ __forceinline__ uint32_t sgpr_value(uint32_t v) {
+  asm("" : "+s"(v));
+  return v;
+}
 __device__ __forceinline__ uint32_t code_pair(uint32_t x, uint32_t mask, uint32_t neg_off) {
-  // one v_and_or_b32 (the exponent constant sits in a VGPR: gfx950 VOP3
-  // encodings take no literal operand)
-  uint32_t r;
-  const uint32_t magic = 0x64006400u;
-  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
-  return pk_add_f16(r, neg_off);
+  uint32_t magic = 0x64006400u;
+  asm("" : "+v"(magic));
+  return pk_add_f16((x & mask) | magic, neg_off);
 }
 
 // Value codes of element group i (8 elements) for tokens 4kq..4kq+3 as the
@@ -217,7 +223,7 @@ struct ValueExpand<4> {
     const bool odd = c & 1;
     const float off = -(1024.0f + (odd ? 16.0f : 1.0f) * kC0);
     const uint32_t neg = f16_pair_bits(off, off);
-    const uint32_t mask = odd ? 0x00F000F0u : 0x000F000Fu;
+    const uint32_t mask = sgpr_value(odd ? 0x00F000F0u : 0x000F000Fu);
     u32x2_t v;
     v[0] = code_pair(pr.x[c >> 1][0], mask, neg);
     v[1] = code_pair(pr.x[c >> 1][1], mask, neg);
@@ -252,7 +258,7 @@ struct ValueExpand<3> {
   __device__ static half4_t get(const Prep &pr, int c) {
     const int src = c < 3 ? 0 : (c < 6 ? 1 : 2);
     const uint32_t m16 = 7u << pos(c);
-    const uint32_t mask = m16 | (m16 << 16);
+    const uint32_t mask = sgpr_value(m16 | (m16 << 16));
     const float off = -(1024.0f + static_cast<float>(1 << pos(c)) * kC0);
     const uint32_t neg = f16_pair_bits(off, off);
     u32x2_t v;
@@ -282,7 +288,7 @@ struct ValueExpand<2> {
   }
   __device__ static half4_t get(const Prep &pr, int c) {
     const uint32_t m16 = 3u << pos(c);
-    const uint32_t mask = m16 | (m16 << 16);
+    const uint32_t mask = sgpr_value(m16 | (m16 << 16));
     const float off = -(1024.0f + static_cast<float>(1 << pos(c)) * kC0);
     const uint32_t neg = f16_pair_bits(off, off);
     u32x2_t v;
@@ -371,7 +377,8 @@ __device__ __forceinline__ float column_sum(float v) {
 template <int N>
 __device__ __forceinline__ uint32_t row_ror(uint32_t v) {
   static_assert(N > 0 && N < 16, "row rotation");
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x120 + N, 0xF, 0xF, false));
+  // every lane has a source lane, so no old value is needed
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x120 + N, 0xF, 0xF, true));
 }
 template <int N>
 __device__ __forceinline__ float row_ror(float v) {
