@@ -178,6 +178,9 @@ def test_decode_argument_errors_before_launch():
     assert _decode(c, q=None) == 1
     assert _decode(c, batch=0) == 0                    # nothing to do
     assert _decode(c, batch=9000) == 3                 # batch above the work-list limit
+    # one pool block of 2 GiB or more (2 heads x 2^24 tokens x 102 bytes)
+    assert _decode(c, bs=1 << 24) == 3 and "2 GiB" in tq.last_error()
+    assert _decode(c, bs=1 << 20, ws=None) == 4        # 214 MB blocks pass that check
 
 
 def test_workspace_size_and_plan():
