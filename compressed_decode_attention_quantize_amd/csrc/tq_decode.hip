@@ -1040,6 +1040,19 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
   const int64_t part0 = static_cast<int64_t>(b) * p.num_q_heads + h * G;
   const int slot = p.max_splits + chunk;
 
+  // A chunk that no query head sees (past the ring's length, or past every
+  // row's causal limit in a prefill chunk) gets the empty partial (m = -inf,
+  // l = 0, acc = 0) without loading anything.
+  bool live = tid < G && n > 0;
+  if (live && p.ring_row_lens) live = p.ring_row_lens[part0 + tid] > c0;
+  if (!__syncthreads_or(live)) {
+    for (int e = tid; e < G * pstride; e += kRingThreads) {
+      const int g = e / pstride, j = e - g * pstride;
+      p.partials[((part0 + g) * p.splits_total + slot) * pstride + j] = j == 0 ? -INFINITY : 0.0f;
+    }
+    return;
+  }
+
   const int rb = p.ring_group > 0 ? b / p.ring_group : b;  // the ring this sequence reads
   const int64_t ring0 = ((static_cast<int64_t>(rb) * p.num_kv_heads + h) * p.ring_cap + c0) * D;
   float qv[kQLoads];
