@@ -93,7 +93,24 @@ __device__ __forceinline__ float load_as_float(const void *base, int dtype, int6
 // ---------------------------------------------------------------------------
 // cross-lane (wave64)
 
-__device__ __forceinline__ float lane_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// v of lane (this lane xor mask). The masks a team uses (1, 2, 4, 8: inside a
+// 16-lane row) are DPP moves, lane c reading lane f(c) of its row: quad_perm
+// [1,0,3,2] and [2,3,0,1] for 1 and 2, row_half_mirror (c xor 7) then
+// quad_perm [3,2,1,0] (xor 3) for 4, row_ror:8 for 8. Other masks go through
+// the LDS permute unit.
+template <int Ctrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Ctrl, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_xor(float v, int mask) {
+  switch (mask) {
+    case 1: return dpp_mov<0xB1>(v);
+    case 2: return dpp_mov<0x4E>(v);
+    case 4: return dpp_mov<0x1B>(dpp_mov<0x141>(v));
+    case 8: return dpp_mov<0x128>(v);
+    default: return __shfl_xor(v, mask, 64);
+  }
+}
 __device__ __forceinline__ float lane_read(float v, int src) { return __shfl(v, src, 64); }
 
 // ---------------------------------------------------------------------------
