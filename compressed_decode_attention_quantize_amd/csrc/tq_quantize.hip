@@ -20,11 +20,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Write `nbytes` (<= 4) little-endian bytes of w at dst (any alignment).
-__device__ __forceinline__ void store_bytes(uint8_t *dst, uint32_t w, int nbytes) {
+// Write the NB (<= 4) little-endian low bytes of w at dst. Fields of an even
+// size start at an even offset of an even-sized slot (slot_size_aligned is
+// even, the pool 16-byte aligned), so they go out as 16-bit stores; a field
+// of 3 bytes can start at an odd offset and goes out byte by byte.
+template <int NB>
+__device__ __forceinline__ void store_field(uint8_t *dst, uint32_t w) {
+  static_assert(NB >= 1 && NB <= 4, "field bytes");
+  if constexpr (NB % 2 == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i < nbytes) dst[i] = static_cast<uint8_t>(w >> (8 * i));
+    for (int i = 0; i < NB; i += 2) *reinterpret_cast<uint16_t *>(dst + i) = static_cast<uint16_t>(w >> (8 * i));
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) dst[i] = static_cast<uint8_t>(w >> (8 * i));
+  }
 }
 
 template <int BITS>
@@ -142,8 +151,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) hi |= float_to_e4m3fn(x[4 + i]) << (8 * i);
     if (write) {
-      store_bytes(dst + 8 * r, lo, 4);
-      store_bytes(dst + 8 * r + 4, hi, 4);
+      store_field<4>(dst + 8 * r, lo);
+      store_field<4>(dst + 8 * r + 4, hi);
     }
   } else {
     const float n2 = team_sumsq<D>(x, team_base);
@@ -176,8 +185,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     }
     const uint32_t w = pack8<KB>(idx);
     if (write) {
-      store_bytes(dst + KB * r, w, KB);
-      if (r == 0) store_bytes(dst + (D * KB) / 8, float_to_f16_bits(n), 2);
+      store_field<KB>(dst + KB * r, w);
+      if (r == 0) store_field<2>(dst + (D * KB) / 8, float_to_f16_bits(n));
     }
   }
 
@@ -206,10 +215,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   const uint32_t wv = pack8<VB>(code);
   if (write) {
     uint8_t *vf = dst + p.key_bytes;
-    store_bytes(vf + VB * r, wv, VB);
+    store_field<VB>(vf + VB * r, wv);
     if (r == 0) {
-      store_bytes(vf + (D * VB) / 8, s16, 2);
-      store_bytes(vf + (D * VB) / 8 + 2, z16, 2);
+      store_field<2>(vf + (D * VB) / 8, s16);
+      store_field<2>(vf + (D * VB) / 8 + 2, z16);
       if (p.slot_bytes > p.key_bytes + (D * VB) / 8 + 4) dst[p.slot_bytes - 1] = 0;
     }
   }
