@@ -34,6 +34,7 @@ TQ_EXPORT tq_status tq_quantize_append(const tq_config *cfg, int layer_idx, cons
   if (st != TQ_OK) return st;
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0 || block_size <= 0)
     return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: negative num_tokens/num_blocks or non-positive heads/block_size");
+  if (num_kv_heads > 65535) return fail(TQ_ERR_UNSUPPORTED, "tq_quantize_append: at most 65535 KV heads");
   if (!valid_dtype(in_dtype)) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: unknown input dtype");
   if (num_tokens == 0) return TQ_OK;
   if (!k || !v || !slot_mapping || !kv_pool) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_append: NULL pointer");
@@ -74,6 +75,7 @@ TQ_EXPORT tq_status tq_ring_flush(const tq_config *cfg, int layer_idx, const uin
   if (batch < 0 || ring_cap <= 0 || num_kv_heads <= 0 || num_blocks < 0 || block_size <= 0 || max_blocks_per_seq < 0)
     return fail(TQ_ERR_INVALID_ARG,
                 "tq_ring_flush: need batch >= 0, ring_cap > 0, num_kv_heads > 0, block_size > 0, non-negative sizes");
+  if (num_kv_heads > 65535) return fail(TQ_ERR_UNSUPPORTED, "tq_ring_flush: at most 65535 KV heads");
   if (batch == 0) return TQ_OK;
   if (!ring_k || !ring_v || !ring_lens || !seq_lens || !block_tables || !kv_pool)
     return fail(TQ_ERR_INVALID_ARG, "tq_ring_flush: NULL pointer");

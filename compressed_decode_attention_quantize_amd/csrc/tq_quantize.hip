@@ -102,11 +102,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   const int r = lane - team * T::kLanes;           // lane within the team
   const int team_base = team * T::kLanes;
   const int lane_in_block = r % T::kBlockLanes;
-  const int64_t vec = (static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave) * T::kPerWave + team;
-  const int64_t nvec = p.num_tokens * p.num_kv_heads;
-  const bool active = team < T::kPerWave && vec < nvec;
-  const int64_t t = active ? vec / p.num_kv_heads : 0;
-  const int h = active ? static_cast<int>(vec - t * p.num_kv_heads) : 0;
+  // grid (token groups, KV heads): the teams of a wave take consecutive
+  // tokens of one head, whose slots are neighbours in a pool block
+  const int64_t tok = (static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave) * T::kPerWave + team;
+  const bool active = team < T::kPerWave && tok < p.num_tokens;
+  const int64_t t = active ? tok : 0;
+  const int h = static_cast<int>(blockIdx.y);
 
   // source element offsets of this (token, head) row, and its slot
   int64_t k_off, v_off, slot = -1;
@@ -139,8 +140,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   }
   const bool write = active && slot >= 0 && slot < p.total_slots;
   if (!write) slot = 0;
-  const int64_t blk = slot / p.block_size;
-  const int64_t off = slot - blk * p.block_size;
+  int64_t blk, off;
+  if ((p.block_size & (p.block_size - 1)) == 0) {
+    // power-of-two block: shift and mask instead of a 64-bit division
+    blk = slot >> __builtin_ctz(static_cast<uint32_t>(p.block_size));
+    off = slot & (p.block_size - 1);
+  } else {
+    blk = slot / p.block_size;
+    off = slot - blk * p.block_size;
+  }
   uint8_t *dst = p.pool + ((blk * p.num_kv_heads + h) * p.block_size + off) * p.slot_bytes;
 
   // ---- keys
@@ -332,12 +340,11 @@ __global__ __launch_bounds__(kThreads) void ring_append_kernel(const uint16_t *k
 template <int D, int KB, int VB>
 int launch_quantize_t(tq_dtype dt, const QuantParams &p, hipStream_t s) {
   using T = Team<D>;
-  const int64_t nvec = p.num_tokens * p.num_kv_heads;
-  const int64_t per_block = (kThreads / 64) * T::kPerWave;
-  const int64_t blocks = (nvec + per_block - 1) / per_block;
+  const int64_t per_block = (kThreads / 64) * T::kPerWave;  // tokens per workgroup
+  const int64_t blocks = (p.num_tokens + per_block - 1) / per_block;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(blocks));
+  if (blocks > 0x7fffffff || p.num_kv_heads > 65535) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(p.num_kv_heads));
   switch (dt) {
     case TQ_F32: hipLaunchKernelGGL((quantize_kernel<D, KB, VB, 0>), grid, dim3(kThreads), 0, s, p); break;
     case TQ_BF16: hipLaunchKernelGGL((quantize_kernel<D, KB, VB, 1>), grid, dim3(kThreads), 0, s, p); break;

@@ -176,6 +176,8 @@ tq_status tq_layer_signs(const tq_config *cfg, int layer_idx, float *signs_out);
  *  slot_mapping  device int64 [num_tokens]; -1 skips the token; ids outside
  *                [0, num_blocks * block_size) are skipped too.
  *  kv_pool       device uint8, layout in the header comment, 16-byte aligned.
+ *  num_kv_heads  at most 65535 (TQ_ERR_UNSUPPORTED otherwise; also for
+ *                tq_ring_flush).
  *
  * Keys (MSE mode): vec_norm = fp16(||k||), u = Pi k / ||k|| with
  * Pi = (1/sqrt(B)) H_B diag(signs), index j = number of midpoints strictly

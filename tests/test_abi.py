@@ -145,6 +145,9 @@ def test_quantize_argument_errors_before_launch():
     # bad dtype
     assert _c_call("tq_quantize_append", cfgp, 0, al, al, 7, 4, 8, 1024, 1024, al, al, 10, 16, None) == 1
     assert "dtype" in tq.last_error()
+    # more KV heads than the launch grid takes
+    assert _c_call("tq_quantize_append", cfgp, 0, al, al, 1, 4, 65536, 1 << 24, 1 << 24, al, al, 10, 16, None) == 3
+    assert "65535" in tq.last_error()
     # zero tokens is a no-op success even with NULL pointers
     assert _c_call("tq_quantize_append", cfgp, 0, None, None, 1, 0, 8, 1024, 1024, None, None, 10, 16, None) == 0
     # a modified config is rejected
