@@ -126,6 +126,24 @@ def test_strided_rows_and_block_size_32():
     assert np.array_equal(pool.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("bs", [7, 24])
+def test_block_size_not_power_of_two(bs):
+    """Slot -> (block, offset) by division rather than shift and mask."""
+    announce(f"quantize block size {bs}")
+    cfg = tq.config_from_preset("turboquant_4bit_nc", 128)
+    ocfg = oracle_cfg(cfg)
+    hkv, n, nb = 3, 200, 40
+    rng = np.random.default_rng(bs)
+    k = rng.standard_normal((n, hkv, 128)).astype(np.float32)
+    v = rng.standard_normal((n, hkv, 128)).astype(np.float32)
+    mapping = rng.permutation(nb * bs)[:n].astype(np.int64)
+    pool = torch.zeros((nb, hkv, bs, cfg.slot_size_aligned), dtype=torch.uint8, device="cuda")
+    tq.quantize_append(cfg, 2, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                       torch.from_numpy(mapping).cuda(), pool)
+    want = oracle_pool(ocfg, 2, k, v, mapping, nb, hkv, bs)
+    assert np.array_equal(pool.cpu().numpy(), want)
+
+
 def test_empty_append_is_noop():
     cfg = tq.config_from_preset("turboquant_3bit_nc", 128)
     pool = torch.full((2, 1, 16, cfg.slot_size_aligned), 7, dtype=torch.uint8, device="cuda")
