@@ -867,6 +867,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     // K slots 8kq..8kq+3 and those of tile i+1 in 8kq+4..8kq+7, each tile's
     // weights masked to its own column group (TL = 1) or both unmasked
     // (TL = 2: every column is in both tiles' group).
+    // A wave in its value phase takes issue priority over the others of its
+    // SIMD until the macro tile ends: it feeds the matrix pipe with a burst of
+    // MFMAs while they do the VALU-heavy key decode (+1-4 % measured).
+    __builtin_amdgcn_s_setprio(1);
     // With partner groups the lo weights of tile t reach group t's partner
     // (the lanes 8 columns away, which hold another tile's scores).
     uint32_t lx[2] = {0u, 0u};
@@ -938,6 +942,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- partial (m, l, acc + zero terms) of query head col
