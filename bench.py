@@ -116,13 +116,21 @@ def cpu_baseline(built, budget_s: float):
 
 def bulk_quantize(built, tq, torch, chunk=65536, reps=5):
     """Quantize-append throughput: `chunk`-token appends into pool 0 (rewriting
-    sequence 0's leading positions), events around each call."""
+    the leading positions of sequences 0, 1, ... until `chunk` tokens, or all
+    of them), events around each call."""
     from workloads import KVSource, slot_ids_for
     w = built.w
-    n = min(chunk, int(built.lens_np[0]))
+    parts, n = [], 0
+    for b in range(len(built.lens_np)):
+        take = min(chunk - n, int(built.lens_np[b]))
+        if take > 0:
+            parts.append(slot_ids_for(built.tables_np, b, 0, take, w.block_size))
+            n += take
+        if n == chunk:
+            break
     src = KVSource(w, "cuda", stream_id=77)
     k, v = src.kv(n)
-    ids = torch.from_numpy(slot_ids_for(built.tables_np, 0, 0, n, w.block_size)).cuda()
+    ids = torch.from_numpy(np.concatenate(parts)).cuda()
     call = tq.prepare_quantize(built.cfg, 0, k, v, ids, built.pools[0])
     for _ in range(2):
         call()
