@@ -436,7 +436,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
