@@ -50,8 +50,10 @@ def _sha(paths):
 
 
 def kernel_source_sha():
+    """Hash of the sources that decide a decode launch's traffic: the
+    kernels and the host-side work plan (range lengths, partial slots)."""
     c = os.path.join(ROOT, "compressed_decode_attention_quantize_amd", "csrc")
-    return _sha([os.path.join(c, "tq_decode.hip"), os.path.join(c, "tq_device.h")])
+    return _sha([os.path.join(c, f) for f in ("tq_decode.hip", "tq_device.h", "tq_host.cpp", "tq_internal.h")])
 
 
 def _traffic(workload_name, per_launch_bytes):

@@ -154,8 +154,12 @@ tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_
   // A wave covers at least min_tokens tokens (except the last wave of a
   // short batch), so a (sequence, KV head) spans at most
   // ceil(len / min_tokens) + 1 waves: one partial slot each.
-  const int min_tokens = split_tokens > 0 ? split_tokens : kMinTokensPerWave;
-  plan->split_tokens = split_tokens;
+  // The automatic range: FP8-key decode streams bytes with little compute
+  // per tile, and measures fastest with ~2 waves per SIMD on 512-token
+  // ranges (fewer range start-ups and partials); the MSE-key decode is
+  // latency-bound and keeps every resident wave busy on 256-token ranges.
+  const int min_tokens = split_tokens > 0 ? split_tokens : (cfg.key_fp8 ? kMinTokensPerWaveFp8 : kMinTokensPerWave);
+  plan->split_tokens = min_tokens;
   plan->max_splits = max_seq_len > 0 ? ceil_div_i(max_seq_len, min_tokens) + 1 : 0;
   plan->splits_total = plan->max_splits + (ring_cap + kRingChunk - 1) / kRingChunk;
   plan->header_bytes = ((16 + 4 * (static_cast<size_t>(batch) + 1) + 255) / 256) * 256;

@@ -87,7 +87,7 @@ struct DecodeParams {
   int32_t max_blocks_per_seq;
   int32_t max_seq_len;
   int32_t ring_cap;
-  int32_t split_tokens;    // minimum tokens per wave (multiple of 16), or 0: 256
+  int32_t split_tokens;    // minimum tokens per wave (multiple of 16)
   int32_t max_splits;      // partial slots per (sequence, q head) for compressed tokens
   int32_t splits_total;    // max_splits + ceil(ring_cap / kRingChunk): slots max_splits.. are the ring's
   int32_t *plan;           // workspace header: [total tiles (int64), active waves, -, tile prefix[batch + 1]]
@@ -155,7 +155,8 @@ struct SplitPlan {
   size_t header_bytes;    // work-division header (16 + 4 (batch + 1), rounded to 256)
   size_t workspace_bytes; // header + partials
 };
-constexpr int kMinTokensPerWave = 256;
+constexpr int kMinTokensPerWave = 256;     // default range of a decode wave (MSE keys)
+constexpr int kMinTokensPerWaveFp8 = 512;  // FP8 keys: fewer, longer ranges
 constexpr int kRingChunk = 32;  // ring tokens per partial slot
 tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_seq_len,
                       int ring_cap, int split_tokens, SplitPlan *plan);

@@ -284,8 +284,9 @@ tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx,
  * Workspace bytes for tq_decode_attention with the same arguments. The
  * decode flattens the batch's (sequence, KV head, 16-token tile) triples and
  * gives every resident wave an equal contiguous range of them, of at least
- * split_tokens tokens (a positive multiple of 16; 0 means 256), so the work
- * is balanced whatever the mix of lengths. The workspace holds a header
+ * split_tokens tokens (a positive multiple of 16; 0 means 512 with FP8 keys
+ * and 256 otherwise), so the work is balanced whatever the mix of lengths.
+ * The workspace holds a header
  * (16 + 4 (batch + 1) bytes, rounded up to 256) and one fp32 partial
  * (max, sum, acc[head_dim]) per (sequence, query head, slot) with
  * ceil(max_seq_len / min tokens) + 1 slots, plus one per 32 ring tokens

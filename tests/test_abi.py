@@ -198,7 +198,10 @@ def test_workspace_size_and_plan():
     assert n == 37
     b, n = tq.decode_workspace_size(c, 4, 8, 0, 0, 0)
     assert n == 0 and b == 256 + 4 * 8 * 1 * 132 * 4
+    # automatic ranges: 512 tokens with FP8 keys, 256 with MSE keys
     _, n_auto = tq.decode_workspace_size(c, 16, 32, 8192)
+    assert n_auto == 17
+    _, n_auto = tq.decode_workspace_size(tq.config_from_preset("turboquant_4bit_nc", 128), 16, 32, 8192)
     assert n_auto == 33
     # the header grows with the batch (tile prefix per sequence)
     b, _ = tq.decode_workspace_size(c, 100, 8, 100, 0, 0)
