@@ -36,6 +36,11 @@ Readings taken where the pages are silent (all also listed in the design doc):
   clamp(rint((v - zero') * (1/scale')), 0, L) computed from the stored
   (fp16-rounded) scale' and zero'; 1/scale' is 0 when scale' is 0; rint is
   half-to-even.
+* Non-finite inputs: min and max skip NaN elements (IEEE minNum / maxNum);
+  a NaN quotient takes code 0; a key coordinate whose rotated value is NaN
+  (a NaN or infinite key makes 1/p zero or NaN) is above no midpoint and
+  gets index 0; fp16 fields of NaN or infinite quantities are the IEEE
+  conversions of those values.
 * Pool layout: [num_blocks][num_kv_heads][block_size][slot_size_aligned]
   bytes; token t goes to block slot_mapping[t] // block_size at offset
   slot_mapping[t] % block_size; slot_mapping -1 means skip.
@@ -168,16 +173,18 @@ def encode_keys_mse(x, cfg: TQConfig, layer_idx: int):
     block = cfg.wht_block
     s = rotation.signs(cfg.seed, layer_idx, cfg.head_dim)
     _, m32 = lloyd_max.tables_f32(cfg.head_dim, cfg.key_mse_bits)
-    n = np.sqrt(sumsq_tree_f32(x, block)).astype(np.float32)
-    norm16 = f32_to_f16_bits(n)
-    z = rotation.butterfly_f32(x * s, block)
-    p = n * np.float32(math.sqrt(block))
-    with np.errstate(divide="ignore"):
-        r = np.where(n == 0, np.float32(0), np.float32(1) / p).astype(np.float32)
-    u = z * r[:, None]
-    # index = number of midpoints strictly below u (searchsorted with side
-    # "left" returns exactly that count for an ascending table)
-    idx = np.searchsorted(m32, u, side="left").astype(np.uint8)
+    # (non-finite keys: the steps below run unchanged; see the header)
+    with np.errstate(invalid="ignore", over="ignore"):
+        n = np.sqrt(sumsq_tree_f32(x, block)).astype(np.float32)
+        norm16 = f32_to_f16_bits(n)
+        z = rotation.butterfly_f32(x * s, block)
+        p = n * np.float32(math.sqrt(block))
+        with np.errstate(divide="ignore"):
+            r = np.where(n == 0, np.float32(0), np.float32(1) / p).astype(np.float32)
+        u = z * r[:, None]
+    # index = number of midpoints strictly below u, counted as written: a NaN
+    # coordinate (from a NaN or infinite key) is below none and gets 0
+    idx = (u[:, :, None] > m32[None, None, :]).sum(axis=2).astype(np.uint8)
     return idx, norm16
 
 
@@ -193,8 +200,11 @@ def encode_values(v, bits: int):
     """Values [N, D] -> (codes [N, D] uint8, scale fp16 bits [N], zero fp16 bits [N])."""
     v = np.asarray(v, dtype=np.float32)
     levels = np.float32(2 ** bits - 1)
-    mn = v.min(axis=1)
-    mx = v.max(axis=1)
+    # minimum and maximum over the elements that are numbers (IEEE 754
+    # minNum / maxNum): a NaN element does not make the scale NaN
+    with np.errstate(invalid="ignore"):
+        mn = np.fmin.reduce(v, axis=1)
+        mx = np.fmax.reduce(v, axis=1)
     scale32 = (mx - mn) / levels
     s16 = f32_to_f16_bits(scale32)
     z16 = f32_to_f16_bits(mn)
@@ -202,7 +212,11 @@ def encode_values(v, bits: int):
     z1 = f16_bits_to_f32(z16)
     with np.errstate(divide="ignore"):
         inv = np.where(s1 == 0, np.float32(0), np.float32(1) / s1).astype(np.float32)
-    q = np.rint((v - z1[:, None]) * inv[:, None])
+    with np.errstate(invalid="ignore"):
+        q = np.rint((v - z1[:, None]) * inv[:, None])
+    # a NaN quotient (NaN element, or an infinite one times 1/inf = 0) takes
+    # the lowest code
+    q = np.where(np.isnan(q), np.float32(0), q)
     codes = np.clip(q, 0, levels).astype(np.uint8)
     return codes, s16, z16
 

@@ -29,6 +29,14 @@ def _inputs(n, hkv, d, seed, dtype):
     v[6] *= 300.0
     k[7] = rng.standard_normal((hkv, d)) * 1e-4
     v[8, :, :] = np.arange(d) % 16          # integer ramp
+    # non-finite elements: a NaN, +inf and -inf in a key row each, then in a
+    # value row each (index 0 for NaN coordinates; min/max skip NaN)
+    k[11, :, 5] = np.nan
+    k[12, :, 7] = np.inf
+    k[13, :, 3] = -np.inf
+    v[14, :, 2] = np.nan
+    v[15, :, 1] = np.inf
+    v[16, :, 0] = -np.inf
     tk = torch.from_numpy(k).to(DT[dtype])
     tv = torch.from_numpy(v).to(DT[dtype])
     return tk, tv, tk.float().numpy(), tv.float().numpy()

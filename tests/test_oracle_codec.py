@@ -170,6 +170,74 @@ def test_zero_key_vector():
     assert (khat == 0).all()
 
 
+def _slot_hex(k_row, v_row, d, kb, vb):
+    cfg = _cfg(d, kb, vb)
+    return X.encode_slots(np.asarray([k_row], np.float32), np.asarray([v_row], np.float32), cfg, 0)[0]
+
+
+def test_non_finite_keys_hand_worked_bytes():
+    """Keys holding a NaN or an infinity, bytes worked out by hand.
+
+    A NaN key makes the norm NaN, so 1/p and every rotated coordinate u are
+    NaN; an infinite key makes the norm infinite, 1/p = 0, and every rotated
+    coordinate of its Hadamard block +-inf, so u = +-inf * 0 = NaN. A NaN lies
+    above no midpoint: index 0 (the count of midpoints strictly below u). The
+    norm field is the fp16 of the norm: 0x7e00 (quiet NaN) or 0x7c00 (+inf).
+    With D = 96 the rotation is three blocks of 32, and an infinity in block
+    0 leaves blocks 1 and 2 finite: there u = z * 0 = +-0, which is above the
+    midpoints below 0 only (the middle midpoint is exactly 0), index
+    2^b / 2 - 1.
+    """
+    rng = np.random.default_rng(17)
+    base64 = rng.standard_normal(64).astype(np.float32)
+    v = np.zeros(64, np.float32)
+    # D = 64, 3-bit: 24 code bytes of index 0, then the norm
+    k = base64.copy()
+    k[5] = np.nan
+    assert _slot_hex(k, v, 64, 3, 4)[:26].tobytes().hex() == "00" * 24 + "007e"
+    k = base64.copy()
+    k[7] = np.inf
+    assert _slot_hex(k, v, 64, 3, 4)[:26].tobytes().hex() == "00" * 24 + "007c"
+    k = base64.copy()
+    k[3] = -np.inf                          # the norm is +inf either way
+    assert _slot_hex(k, v, 64, 3, 4)[:26].tobytes().hex() == "00" * 24 + "007c"
+    # D = 96, infinity at element 7 (block 0)
+    base96 = rng.standard_normal(96).astype(np.float32)
+    v96 = np.zeros(96, np.float32)
+    k = base96.copy()
+    k[7] = np.inf
+    # 3-bit: elements 0..31 index 0 (12 bytes); 32..95 index 3 = 0b011, eight
+    # elements per 24 bits: sum_j 3 << 3j = 0x6db6db, little-endian db b6 6d
+    assert _slot_hex(k, v96, 96, 3, 4)[:38].tobytes().hex() == "00" * 12 + "dbb66d" * 8 + "007c"
+    # 4-bit: index 7 in two nibbles per byte
+    assert _slot_hex(k, v96, 96, 4, 4)[:50].tobytes().hex() == "00" * 16 + "77" * 32 + "007c"
+
+
+def test_non_finite_values_hand_worked_bytes():
+    """Values holding a NaN or an infinity, bytes worked out by hand.
+
+    min and max skip a NaN element, so the integer ramp 0..15 with one NaN
+    keeps scale 1 and zero 0 (fp16 0x3c00, 0x0000), and the NaN element takes
+    code 0. An infinity makes the scale infinite (0x7c00) and 1/scale' = 0, so
+    every code is 0 (finite elements: rint(+-0); the infinite one: inf * 0 =
+    NaN -> 0); -inf is also the zero point (0xfc00).
+    """
+    k = np.ones(64, np.float32)
+    ramp = (np.arange(64) % 16).astype(np.float32)
+    off = 26                                 # value field after the 3-bit key field at D = 64
+    v = ramp.copy()
+    v[5] = np.nan
+    # codes 0..15 pack as 10 32 54 76 98 ba dc fe; code 5 -> 0 makes byte 2 0x04
+    want = "1032047698badcfe" + "1032547698badcfe" * 3 + "003c" + "0000"
+    assert _slot_hex(k, v, 64, 3, 4)[off:off + 36].tobytes().hex() == want
+    v = ramp.copy()
+    v[1] = np.inf
+    assert _slot_hex(k, v, 64, 3, 4)[off:off + 36].tobytes().hex() == "00" * 32 + "007c" + "0000"
+    v = ramp.copy()
+    v[0] = -np.inf
+    assert _slot_hex(k, v, 64, 3, 4)[off:off + 36].tobytes().hex() == "00" * 32 + "007c" + "00fc"
+
+
 def test_norm_correction_changes_no_bytes():
     rng = np.random.default_rng(5)
     k = rng.standard_normal((64, 128)).astype(np.float32)
