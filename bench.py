@@ -5,7 +5,7 @@ token per sequence into the paged pool, then fused decode attention over
 every sequence's full context. Inputs are seeded synthetic data already
 resident in HBM (see workloads/). Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload k8v4]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4bit_nc]
 
 Timing, after 0.25 s of back-to-back decode launches (clock ramp) and W
 warm-up steps, in this order:
@@ -70,21 +70,73 @@ def _traffic(workload_name, per_launch_bytes):
     return entry.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(built, budget_s: float):
-    """The oracle's decode attention timed on host cores over a bounded
-    sample (whole sequences of the same workload, oracle-encoded from the same
-    K/V), in KV tokens per second."""
+def host_description():
+    """The host CPU as the oracle baseline ran on it: model name, the
+    machine's logical CPU count, and the CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable}
+
+
+# Worker processes of the all-cores oracle baseline: at most this many (the
+# host share of one GPU), each single-threaded.
+CPU_WORKERS_MAX = 16
+
+
+def _oracle_decode_worker(job):
+    """One single-threaded worker of the all-cores baseline: the oracle's
+    decode of the sample sequence, repeated until `budget_s` has passed.
+    Returns (KV tokens attended, seconds)."""
+    q, pool, table, n, ring, cfg_fields, budget_s, start_at = job
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as OA
+    from oracle import config as OC
+
+    ocfg = OC.TQConfig(**cfg_fields)
+    tokens = 0
+    with threadpool_limits(limits=1):
+        while time.time() < start_at:       # all workers start together
+            time.sleep(0.001)
+        t0 = time.perf_counter()
+        while True:
+            OA.decode_attention(q, pool, table, [n], ocfg, 0, **ring)
+            tokens += n + (int(ring["ring_lens"][0]) if ring else 0)
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                return tokens, el
+
+
+def cpu_baseline(built, budget_s: float):
+    """The oracle's decode attention timed on host cores over a bounded
+    sample (one whole sequence of the same workload, oracle-encoded from the
+    same K/V), in KV tokens per second: (i) one core, one process; (ii) all
+    usable cores (at most CPU_WORKERS_MAX), one single-threaded worker process
+    per core, each decoding the sample sequence repeatedly. The decode cost
+    is the same for every sequence of a uniform workload, so (ii) is the
+    throughput of sharding the batch by sequence."""
+    import multiprocessing as mp
+
     from oracle import codec as OX
     from oracle import config as OC
 
     w = built.w
     cfg = built.cfg
-    ocfg = OC.TQConfig(head_dim=cfg.head_dim, key_quant_bits=cfg.key_quant_bits,
-                       value_quant_bits=cfg.value_quant_bits, seed=int(cfg.seed),
-                       norm_correction=bool(cfg.norm_correction))
+    cfg_fields = dict(head_dim=cfg.head_dim, key_quant_bits=cfg.key_quant_bits,
+                      value_quant_bits=cfg.value_quant_bits, seed=int(cfg.seed),
+                      norm_correction=bool(cfg.norm_correction))
+    ocfg = OC.TQConfig(**cfg_fields)
     b = min(built.captured)
     k, v = built.captured[b]
     n = k.shape[0]
@@ -100,20 +152,25 @@ def cpu_baseline(built, budget_s: float):
         ring = dict(ring_k=built.ring_k[b:b + 1].float().cpu().numpy(),
                     ring_v=built.ring_v[b:b + 1].float().cpu().numpy(),
                     ring_lens=np.array([w.ring]))
-    tokens = 0
-    reps = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            OA.decode_attention(q, pool, table, [n], ocfg, 0, **ring)
-            tokens += n + w.ring
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
-                break
-    return {"value": tokens / el, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"sequence {b} ({n} compressed + {w.ring} ring tokens, {w.num_q_heads} q heads) "
-                      f"decoded {reps}x in {el:.1f} s, numpy single-threaded"}
+    host = host_description()
+    # (i) one core, in this process
+    tok1, el1 = _oracle_decode_worker((q, pool, table, n, ring, cfg_fields, budget_s, 0.0))
+    # (ii) all cores: fresh interpreters (spawn), none of which touches the GPU
+    nw = max(1, min(CPU_WORKERS_MAX, host["usable_cpus"]))
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(nw) as pool_:
+        start_at = time.time() + 5.0 + 0.1 * nw    # after every worker has imported numpy
+        res = pool_.map(_oracle_decode_worker,
+                        [(q, pool, table, n, ring, cfg_fields, budget_s, start_at)] * nw, chunksize=1)
+    tok_all = sum(t for t, _ in res)
+    el_all = max(e for _, e in res)
+    seq = f"sequence {b} ({n} compressed + {w.ring} ring tokens, {w.num_q_heads} q heads)"
+    return {"value": tok1 / el1, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{seq} decoded {tok1 // max(n + w.ring, 1)}x in {el1:.1f} s, numpy single-threaded",
+            "all_cores": {"value": tok_all / el_all, "unit": "KV tokens/s", "cores": nw,
+                          "sample": f"{seq} decoded {tok_all // max(n + w.ring, 1)}x by {nw} single-threaded "
+                                    f"worker processes over {el_all:.1f} s"},
+            "host": host}
 
 
 def bulk_quantize(built, tq, torch, chunk=65536, reps=5):
@@ -289,6 +346,29 @@ def concurrent_prefill(built, tq, torch, steps, reps=10):
             "overlapped_GBps": (pbytes + dbytes) / (both_ms / 1e3) / 1e9}
 
 
+# The pages' own figures for the four presets (vLLM API page
+# "vllm.model_executor.layers.quantization.turboquant", TurboQuantConfig
+# docstring, named presets): KV compression and perplexity change, as quoted
+# (model and data unnamed). Context for the measurements, not a target.
+PAGE_PRESET_FIGURES = {
+    "turboquant_k8v4": {"compression_quoted": "2.6x", "ppl_delta_quoted": "+1.17%"},
+    "turboquant_4bit_nc": {"compression_quoted": "3.8x", "ppl_delta_quoted": "+2.71%"},
+    "turboquant_k3v4_nc": {"compression_quoted": "~3.5x", "ppl_delta_quoted": "+10.63%"},
+    "turboquant_3bit_nc": {"compression_quoted": "4.9x", "ppl_delta_quoted": "+20.59%"},
+}
+
+
+def page_context(w, cfg):
+    """The preset's quoted figures beside the ratio its slot size gives
+    (bf16 K + V = 4 D bytes per token and head, over slot_size_aligned)."""
+    out = {"slot_bytes": cfg.slot_size_aligned,
+           "compression_vs_bf16_from_slot_size": round(4 * w.head_dim / cfg.slot_size_aligned, 3)}
+    if w.preset in PAGE_PRESET_FIGURES:
+        out.update(PAGE_PRESET_FIGURES[w.preset])
+        out["source"] = "vLLM API page TurboQuantConfig docstring, named presets (model and data unnamed)"
+    return out
+
+
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 matrix peak, published
 
 
@@ -431,7 +511,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="k8v4")
+    ap.add_argument("--workload", default="4bit_nc")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -574,6 +654,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "frac_of_copy": achieved / copy["GBps"]},
         **extra,
+        "page_context": page_context(w, cfg),
         "wall_s_timed": wall,
         "library": tq.version(),
     }

@@ -245,6 +245,19 @@ def _stream_ptr(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _alloc_stream(stream, device):
+    """Context for allocating a call's own out / workspace tensors: on the
+    stream the call runs on. torch's caching allocator hands a freed block
+    only to later allocations on the stream it was allocated on, so memory
+    the kernels of a caller-chosen stream still use is never given to work
+    on another stream."""
+    import contextlib
+    torch = _torch()
+    if stream is None:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device))
+
+
 def quantize_append(cfg: Config, layer_idx: int, k, v, slot_mapping, kv_pool, stream=None) -> None:
     """k, v: [T, Hkv, D] (or [T, Hkv*D] rows with a token stride) float32/bf16/f16
     with the head and element dims contiguous; slot_mapping int64 [T];
@@ -371,14 +384,15 @@ def decode_attention(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_
             raise ValueError(f"ring_k/ring_v must be contiguous bf16 [B, {hkv}, ring_cap, {d}]")
         ring_cap = ring_k.shape[2]
         rk, rv, rl = ring_k.data_ptr(), ring_v.data_ptr(), ring_lens.data_ptr()
-    if out is None:
-        out = torch.empty((bsz, hq, d), dtype=torch.float32, device=q.device)
+    need, _ = decode_workspace_size(cfg, bsz, hq, max_seq_len, ring_cap, split_tokens)
+    with _alloc_stream(stream, q.device):
+        if out is None:
+            out = torch.empty((bsz, hq, d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _dev(out, "out", torch.float32)
     if out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out must be contiguous float32 like q")
-    need, _ = decode_workspace_size(cfg, bsz, hq, max_seq_len, ring_cap, split_tokens)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
     s = stream if stream is not None else _stream_ptr(q)
     _check(_lib.tq_decode_attention(ctypes.byref(cfg), layer_idx, q.data_ptr(), _dtype_code(q), bsz, hq, hkv,
@@ -423,12 +437,13 @@ def prefill_attention(cfg: Config, layer_idx: int, q, k_chunk, v_chunk, cu_chunk
         raise ValueError("cu_chunk must be [B + 1], hist_lens [B], block_tables contiguous [B, max_blocks]")
     if kv_pool.dim() != 4 or kv_pool.shape[3] != cfg.slot_size_aligned or not kv_pool.is_contiguous():
         raise ValueError("kv_pool must be contiguous [num_blocks, Hkv, block_size, slot_size_aligned]")
-    if out is None:
-        out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
-    _dev(out, "out", torch.float32)
     need = prefill_workspace_size(cfg, bsz, hq, hkv, max_chunk, max_hist, block_tables.shape[1], _dtype_code(q))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    with _alloc_stream(stream, q.device):
+        if out is None:
+            out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(out, "out", torch.float32)
     _dev(workspace, "workspace", torch.uint8)
     s = stream if stream is not None else _stream_ptr(q)
     _check(_lib.tq_prefill_attention(ctypes.byref(cfg), layer_idx, q.data_ptr(), _dtype_code(q), k_chunk.data_ptr(),
@@ -449,10 +464,11 @@ def dequant(cfg: Config, layer_idx: int, kv_pool, slot_ids, k_out=None, v_out=No
     n = slot_ids.numel()
     hkv = kv_pool.shape[1]
     shape = (n, hkv, cfg.head_dim)
-    if k_out is None:
-        k_out = torch.empty(shape, dtype=torch.float32, device=kv_pool.device)
-    if v_out is None:
-        v_out = torch.empty(shape, dtype=torch.float32, device=kv_pool.device)
+    with _alloc_stream(stream, kv_pool.device):
+        if k_out is None:
+            k_out = torch.empty(shape, dtype=torch.float32, device=kv_pool.device)
+        if v_out is None:
+            v_out = torch.empty(shape, dtype=torch.float32, device=kv_pool.device)
     s = stream if stream is not None else _stream_ptr(kv_pool)
     _check(_lib.tq_dequant(ctypes.byref(cfg), layer_idx, kv_pool.data_ptr(), kv_pool.shape[0], hkv,
                            kv_pool.shape[2], slot_ids.data_ptr(), n, k_out.data_ptr(), v_out.data_ptr(), s))
@@ -503,10 +519,11 @@ def prepare_decode(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_le
     bsz, hq, d = q.shape
     ring_cap = 0 if ring_k is None else ring_k.shape[2]
     need, _ = decode_workspace_size(cfg, bsz, hq, max_seq_len, ring_cap, split_tokens)
-    if out is None:
-        out = torch.empty((bsz, hq, d), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    with _alloc_stream(stream, q.device):
+        if out is None:
+            out = torch.empty((bsz, hq, d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     decode_attention(cfg, layer_idx, q, kv_pool, block_tables, seq_lens, max_seq_len, ring_k, ring_v,
                      ring_lens, softmax_scale, out, workspace, split_tokens, stream)
     s = stream if stream is not None else _stream_ptr(q)

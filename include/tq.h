@@ -26,9 +26,11 @@
  * Conventions for every function:
  *  - Returns a tq_status; never throws or aborts. On failure nothing is
  *    enqueued and tq_last_error() describes the problem.
- *  - Device pointers are caller-owned; the library allocates no device memory
- *    and keeps no mutable global state, so calls are reentrant and may run
- *    concurrently on different streams when they write disjoint memory.
+ *  - Device pointers are caller-owned; the library allocates no device memory.
+ *    Its only mutable global state is a process-wide, mutex-guarded cache of
+ *    the decode kernels' resident workgroups per (kernel, device), filled on
+ *    first use; calls are reentrant and may run concurrently on different
+ *    streams when they write disjoint memory.
  *  - GPU calls are asynchronous and ordered on `stream` (a hipStream_t passed
  *    as void*; NULL = the default stream).
  *  - Scalars and null pointers are validated on the host. Device contents

@@ -59,3 +59,36 @@ def per_head_rel_l2(got, want):
 
 def as_f32_host(t) -> np.ndarray:
     return t.float().cpu().numpy()
+
+
+def attention_conditioning(q, pool, tables, lens, ocfg, layer, ring_k=None, ring_v=None, ring_lens=None):
+    """Per (sequence, query head): the condition number of the softmax-
+    weighted value sum, kappa = sum_t p_t |v_t| / |sum_t p_t v_t| (float64,
+    from the oracle's dequantized cache), and the number of attended tokens
+    n. A relative perturbation e of every term moves the output by at most
+    kappa * e relative to its norm."""
+    import math
+    from oracle import attention as OA
+    q = np.asarray(q, np.float64)
+    b_s, hq, d = q.shape
+    hkv = pool.shape[1]
+    g = hq // hkv
+    kap = np.zeros((b_s, hq))
+    n_tok = np.zeros(b_s, np.int64)
+    for b in range(b_s):
+        for h in range(hkv):
+            k, v = OA.sequence_kv(pool, tables[b], int(lens[b]), h, ocfg, layer)
+            if ring_lens is not None and int(ring_lens[b]) > 0:
+                r = int(ring_lens[b])
+                k = np.concatenate([k, np.asarray(ring_k[b, h, :r], np.float64)])
+                v = np.concatenate([v, np.asarray(ring_v[b, h, :r], np.float64)])
+            n_tok[b] = k.shape[0]
+            if k.shape[0] == 0:
+                continue
+            s = (q[b, h * g:(h + 1) * g] @ k.T) / math.sqrt(d)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ v
+            vn = np.linalg.norm(v, axis=1)
+            kap[b, h * g:(h + 1) * g] = (p @ vn) / np.linalg.norm(o, axis=1)
+    return kap, n_tok

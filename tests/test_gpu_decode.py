@@ -196,22 +196,49 @@ def test_layer_adaptive_key_bits():
         assert per_head_rel_l2(out.cpu().numpy(), want) <= ATTN_RTOL
 
 
+def split_difference_bound(kappa, n):
+    """Largest relative L2 difference between two split choices of one
+    (sequence, query head) that the decode arithmetic allows.
+
+    The scores s_t do not depend on the split (the same f16 operands summed
+    over D in the same MFMA order). What changes is (i) the running maximum
+    each weight is taken against: p_t = exp2(s_t - m) rounds with v_exp_f32's
+    1 ulp (2^-23 relative), the weight p_t s'_t is carried as f16 hi + lo
+    parts (2^-22 relative); and (ii) the order of the fp32 sums over the
+    tokens (partials, merge). Under the probabilistic rounding model a sum
+    of n terms errs by at most lambda sqrt(n) u of the sum of magnitudes
+    (u = 2^-24), taken with lambda = 2 for each of the two runs. Relative
+    term errors e move the output by at most kappa e relative to its norm,
+    so the two runs differ by at most kappa (2 (2^-22 + 2^-23) + 4 sqrt(n) u)."""
+    u = 2.0 ** -24
+    return kappa * (2 * (2.0 ** -22 + 2.0 ** -23) + 4 * np.sqrt(n) * u)
+
+
 def test_split_invariance_and_determinism():
+    from tests.gpu_common import attention_conditioning, rel_l2
     announce("decode split invariance")
     lens = [1777, 900, 3]
     cfg, ocfg, pool_np, tables, q, ring = _scenario(128, 4, 4, True, 16, 4, lens, [40, 128, 0], 128, seed=4)
     runs = [_run(cfg, ocfg, pool_np, tables, lens, q, ring, split_tokens=s) for s in (16, 64, 256, 2048)]
     outs = [r[0] for r in runs]
-    # every split choice meets the oracle bound; between themselves they
-    # differ only by fp32 summation order (weights are carried to ~22 bits)
+    # every split choice meets the oracle bound
     for got, want in runs:
         err = per_head_rel_l2(got, want)
         announce(f"  rel L2 {err:.2e}")
         assert err <= ATTN_RTOL
+    # between themselves they differ within the bound the arithmetic allows
+    kappa, n_tok = attention_conditioning(q.float().numpy(), pool_np, tables, lens, ocfg, 0,
+                                          ring[0].float().numpy(), ring[1].float().numpy(), ring[2])
     for o in outs[1:]:
-        d = per_head_rel_l2(o, outs[0])
-        announce(f"  split-to-split {d:.2e}")
-        assert d <= 1e-4
+        worst = worst_ratio = 0.0
+        for b in range(len(lens)):
+            for g in range(o.shape[1]):
+                d = rel_l2(o[b, g], outs[0][b, g])
+                bound = split_difference_bound(kappa[b, g], n_tok[b])
+                worst = max(worst, d)
+                worst_ratio = max(worst_ratio, d / bound)
+                assert d <= bound, (b, g, d, bound, kappa[b, g])
+        announce(f"  split-to-split {worst:.2e} (at most {worst_ratio:.2f} of the per-head bound)")
     again = _run(cfg, ocfg, pool_np, tables, lens, q, ring, split_tokens=64)[0]
     assert np.array_equal(again.view(np.uint32), outs[1].view(np.uint32))
 
