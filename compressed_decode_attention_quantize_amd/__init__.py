@@ -350,14 +350,9 @@ def decode_workspace_size(cfg: Config, batch: int, num_q_heads: int, max_seq_len
     return b.value, n.value
 
 
-def decode_attention(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_lens, max_seq_len: int,
-                     ring_k=None, ring_v=None, ring_lens=None, softmax_scale: float = 0.0,
-                     out=None, workspace=None, split_tokens: int = 0, stream=None):
-    """q [B, Hq, D] (f32/bf16/f16, contiguous) -> out [B, Hq, D] float32.
-
-    block_tables int32 [B, max_blocks]; seq_lens int32 [B]; ring_k/ring_v
-    bf16 [B, Hkv, ring_cap, D] with ring_lens int32 [B], or None.
-    """
+def _decode_args(cfg: Config, q, kv_pool, block_tables, seq_lens, ring_k, ring_v, ring_lens):
+    """Checks the tensors of a decode call; returns (batch, Hq, Hkv, D,
+    ring_cap, ring pointers)."""
     torch = _torch()
     _dev(q, "q")
     _dev(kv_pool, "kv_pool", torch.uint8)
@@ -384,6 +379,20 @@ def decode_attention(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_
             raise ValueError(f"ring_k/ring_v must be contiguous bf16 [B, {hkv}, ring_cap, {d}]")
         ring_cap = ring_k.shape[2]
         rk, rv, rl = ring_k.data_ptr(), ring_v.data_ptr(), ring_lens.data_ptr()
+    return bsz, hq, hkv, d, ring_cap, rk, rv, rl
+
+
+def decode_attention(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_lens, max_seq_len: int,
+                     ring_k=None, ring_v=None, ring_lens=None, softmax_scale: float = 0.0,
+                     out=None, workspace=None, split_tokens: int = 0, stream=None):
+    """q [B, Hq, D] (f32/bf16/f16, contiguous) -> out [B, Hq, D] float32.
+
+    block_tables int32 [B, max_blocks]; seq_lens int32 [B]; ring_k/ring_v
+    bf16 [B, Hkv, ring_cap, D] with ring_lens int32 [B], or None.
+    """
+    torch = _torch()
+    bsz, hq, hkv, d, ring_cap, rk, rv, rl = _decode_args(cfg, q, kv_pool, block_tables, seq_lens,
+                                                         ring_k, ring_v, ring_lens)
     need, _ = decode_workspace_size(cfg, bsz, hq, max_seq_len, ring_cap, split_tokens)
     with _alloc_stream(stream, q.device):
         if out is None:

@@ -270,10 +270,10 @@ TQ_EXPORT tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx, co
   p.max_seq_len = max_hist;
   p.ring_cap = max_chunk;
   p.split_tokens = L.plan.split_tokens;
-  p.max_splits = L.plan.max_splits;
-  p.splits_total = L.plan.splits_total;
+  p.ring_chunks = L.plan.ring_chunks;
   p.plan = reinterpret_cast<int32_t *>(ws + L.dec);
   p.partials = reinterpret_cast<float *>(ws + L.dec + L.plan.header_bytes);
+  p.ring_partials = reinterpret_cast<float *>(ws + L.dec + L.plan.ring_offset);
   p.slot_bytes = cfg->slot_size_aligned;
   p.key_bytes = cfg->key_packed_size;
   p.norm_correction = cfg->norm_correction;
@@ -323,45 +323,46 @@ TQ_EXPORT tq_status tq_dequant(const tq_config *cfg, int layer_idx, const uint8_
   return TQ_OK;
 }
 
-TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, const void *q, tq_dtype q_dtype,
-                                        int batch, int num_q_heads, int num_kv_heads, const uint8_t *kv_pool,
-                                        int64_t num_blocks, int block_size, const int32_t *block_tables,
-                                        int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len,
-                                        const void *ring_k, const void *ring_v, const int32_t *ring_lens,
-                                        int ring_cap, float softmax_scale, float *out, void *workspace,
-                                        size_t workspace_bytes, int split_tokens, void *stream) {
+namespace {
+
+// Validates a decode call and fills everything but the workspace pointers.
+// *run is false when there is nothing to launch (batch 0).
+tq_status decode_setup(const char *fn, const tq_config *cfg, int layer_idx, const void *q, tq_dtype q_dtype,
+                       int batch, int num_q_heads, int num_kv_heads, const uint8_t *kv_pool, int64_t num_blocks,
+                       int block_size, const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens,
+                       int max_seq_len, const void *ring_k, const void *ring_v, const int32_t *ring_lens,
+                       int ring_cap, float softmax_scale, float *out, int split_tokens, DecodeParams *pp,
+                       SplitPlan *plan, bool *run) {
+  *run = false;
+  const std::string f(fn);
   tq_status st = check_config(cfg);
   if (st != TQ_OK) return st;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: need batch >= 0 and num_q_heads a positive multiple of num_kv_heads");
+    return fail(TQ_ERR_INVALID_ARG, f + ": need batch >= 0 and num_q_heads a positive multiple of num_kv_heads");
   if (batch > 8192)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: at most 8192 sequences per call");
+    return fail(TQ_ERR_UNSUPPORTED, f + ": at most 8192 sequences per call");
   if (num_q_heads / num_kv_heads > 16)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: at most 16 query heads per KV head");
+    return fail(TQ_ERR_UNSUPPORTED, f + ": at most 16 query heads per KV head");
   if (block_size <= 0 || block_size % 16 != 0)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: block_size must be a positive multiple of 16");
+    return fail(TQ_ERR_UNSUPPORTED, f + ": block_size must be a positive multiple of 16");
   if (static_cast<int64_t>(num_kv_heads) * block_size * cfg->slot_size_aligned > INT32_MAX)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attention: a pool block (num_kv_heads * block_size * slot bytes) must be below 2 GiB");
+    return fail(TQ_ERR_UNSUPPORTED, f + ": a pool block (num_kv_heads * block_size * slot bytes) must be below 2 GiB");
   if (max_seq_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0 || ring_cap < 0)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: negative size argument");
-  if (!valid_dtype(q_dtype)) return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: unknown q dtype");
+    return fail(TQ_ERR_INVALID_ARG, f + ": negative size argument");
+  if (!valid_dtype(q_dtype)) return fail(TQ_ERR_INVALID_ARG, f + ": unknown q dtype");
   const bool has_ring = ring_k != nullptr || ring_v != nullptr;
   if (has_ring && (!ring_k || !ring_v || !ring_lens || ring_cap <= 0))
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: ring needs ring_k, ring_v, ring_lens and ring_cap > 0");
+    return fail(TQ_ERR_INVALID_ARG, f + ": ring needs ring_k, ring_v, ring_lens and ring_cap > 0");
   if (!has_ring && ring_cap != 0)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: ring_cap must be 0 without a ring");
+    return fail(TQ_ERR_INVALID_ARG, f + ": ring_cap must be 0 without a ring");
   if (batch == 0) return TQ_OK;
   if (!q || !kv_pool || !block_tables || !seq_lens || !out)
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: NULL pointer");
+    return fail(TQ_ERR_INVALID_ARG, f + ": NULL pointer");
   if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || (has_ring && (!aligned16(ring_k) || !aligned16(ring_v))))
-    return fail(TQ_ERR_INVALID_ARG, "tq_decode_attention: q, kv_pool, out, ring_k and ring_v must be 16-byte aligned");
-  SplitPlan plan;
-  st = plan_decode(*cfg, batch, num_q_heads, max_seq_len, ring_cap, split_tokens, &plan);
+    return fail(TQ_ERR_INVALID_ARG, f + ": q, kv_pool, out, ring_k and ring_v must be 16-byte aligned");
+  st = plan_decode(*cfg, batch, num_q_heads, max_seq_len, ring_cap, split_tokens, plan);
   if (st != TQ_OK) return st;
-  if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned16(workspace))
-    return fail(TQ_ERR_WORKSPACE, "tq_decode_attention: workspace must be 16-byte aligned and hold " +
-                                      std::to_string(plan.workspace_bytes) + " bytes");
-  DecodeParams p;
+  DecodeParams &p = *pp;
   std::memset(&p, 0, sizeof(p));
   p.q = q;
   p.pool = kv_pool;
@@ -379,11 +380,8 @@ TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, con
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.max_seq_len = max_seq_len;
   p.ring_cap = has_ring ? ring_cap : 0;
-  p.split_tokens = plan.split_tokens;
-  p.max_splits = plan.max_splits;
-  p.splits_total = plan.splits_total;
-  p.plan = static_cast<int32_t *>(workspace);
-  p.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.header_bytes);
+  p.split_tokens = plan->split_tokens;
+  p.ring_chunks = plan->ring_chunks;
   p.slot_bytes = cfg->slot_size_aligned;
   p.key_bytes = cfg->key_packed_size;
   p.norm_correction = cfg->norm_correction;
@@ -393,6 +391,37 @@ TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, con
   p.centroid_scale = cfg->centroid_scale;
   layer_sign_mask(*cfg, layer_idx, p.sign_words);
   for (int i = 0; i < 16; ++i) p.centroids[i] = cfg->centroids[i];
+  *run = true;
+  return TQ_OK;
+}
+
+void bind_workspace(DecodeParams &p, const SplitPlan &plan, void *workspace) {
+  char *ws = static_cast<char *>(workspace);
+  p.plan = reinterpret_cast<int32_t *>(ws);
+  p.partials = reinterpret_cast<float *>(ws + plan.header_bytes);
+  p.ring_partials = reinterpret_cast<float *>(ws + plan.ring_offset);
+}
+
+}  // namespace
+
+TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, const void *q, tq_dtype q_dtype,
+                                        int batch, int num_q_heads, int num_kv_heads, const uint8_t *kv_pool,
+                                        int64_t num_blocks, int block_size, const int32_t *block_tables,
+                                        int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len,
+                                        const void *ring_k, const void *ring_v, const int32_t *ring_lens,
+                                        int ring_cap, float softmax_scale, float *out, void *workspace,
+                                        size_t workspace_bytes, int split_tokens, void *stream) {
+  DecodeParams p;
+  SplitPlan plan;
+  bool run = false;
+  tq_status st = decode_setup("tq_decode_attention", cfg, layer_idx, q, q_dtype, batch, num_q_heads, num_kv_heads,
+                              kv_pool, num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
+                              ring_k, ring_v, ring_lens, ring_cap, softmax_scale, out, split_tokens, &p, &plan, &run);
+  if (st != TQ_OK || !run) return st;
+  if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned16(workspace))
+    return fail(TQ_ERR_WORKSPACE, "tq_decode_attention: workspace must be 16-byte aligned and hold " +
+                                      std::to_string(plan.workspace_bytes) + " bytes");
+  bind_workspace(p, plan, workspace);
   const int err = launch_decode(*cfg, q_dtype, p, stream);
   if (err != hipSuccess) return hip_fail("tq_decode_attention launch", err);
   return TQ_OK;

@@ -88,7 +88,7 @@ struct Geo {
   // up to 7 bytes past a field, rounded to 16 bytes
   static constexpr int kTileBuf = ((kTileBytes + 16) + 15) / 16 * 16;
   // one wave's LDS: `bufs` tile buffers, or the queries
-  static constexpr int scratch_bytes(int bufs) { return bufs * kTileBuf > kQBytes ? bufs * kTileBuf : kQBytes; }
+  static constexpr int stage_bytes(int bufs) { return bufs * kTileBuf > kQBytes ? bufs * kTileBuf : kQBytes; }
   static constexpr int kLut = KB == 4 ? 256 : (KB == 3 ? 64 : 1);
   // every lane's key bytes, and every value code group, start on a word
   static constexpr bool kKeyAligned = kSlot % 4 == 0 && kLaneKeyBytes % 4 == 0;
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int kBufs = kValLds ? NT + 1 : 2;
 
   __shared__ uint32_t lut[GE::kLut];
-  __shared__ __align__(16) uint32_t scratch[kWaves][GE::scratch_bytes(kBufs) / 4];
+  __shared__ __align__(16) uint32_t stage[kWaves][GE::stage_bytes(kBufs) / 4];
   // per-token scalars of the macro tile: norm * scale (< 0: masked), s', z' + c0 s', ||c||^2;
   // plane 4 takes the writes of lanes that hold nothing for a plane
   __shared__ __align__(16) float tokf[kWaves][5][NT][16];
@@ -445,8 +445,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   // that order; wave w of the W active waves takes the contiguous range
   // [w T / W, (w+1) T / W) of the T tiles (at least min_tiles each), so every
   // wave streams the same number of tiles whatever the length mix. A wave
-  // writes one partial per (sequence, KV head) segment it covers; the
-  // segment's slot is its wave index minus the first wave of the segment.
+  // writes one partial per (sequence, KV head) segment it covers, at row
+  // w + s of the partials (s = b Hkv + h): the waves' ranges follow each
+  // other, so a wave's segments and the next wave's start at or after its
+  // last one, and the rows are distinct.
   extern __shared__ int32_t seq_prefix[];  // [batch + 1]: tiles of sequences < b
   __shared__ int32_t scan_s[64 * kWaves];
   const int tid = threadIdx.x;
@@ -507,7 +509,6 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   const long long seg_start = seg0 + static_cast<long long>(h) * nb;   // first tile of (b, h)
   const long long seg_stop = seg_start + nb;
   const long long run_end = seg_stop < f_end ? seg_stop : f_end;
-  const int slot = w - first_wave(seg_start, total, active);
   const int begin = static_cast<int>(f - seg_start) * kTile;
   // The range's first loads go out together: its length, the block ids of
   // its first 64 blocks (lane i: logical block blk_base + i) and, below, the
@@ -520,10 +521,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   int nx_off = begin - nx_blk * p.block_size;
   int blk_base = nx_blk;
   int blk_lane = blk_base + lane < p.max_blocks_per_seq ? bt_row[blk_base + lane] : 0;
-  float *part_base = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + h * G) * p.splits_total * pstride +
-                     static_cast<int64_t>(slot) * pstride;
+  // this wave's partial row of segment (b, h): row w + s, s = b Hkv + h
+  float *part_base = p.partials + (static_cast<int64_t>(w) + static_cast<int64_t>(b) * Hkv + h) * G * pstride;
 
-  uint32_t *scr = scratch[wave];  // this wave's LDS: queries, then the staged tile
+  uint32_t *scr = stage[wave];  // this wave's LDS: queries, then the staged tile
 
   // ---- rotated queries as f16 hi + lo parts, in the MFMA B-operand layout.
   // Column n of the score MFMA is query head n % GP of tile slot n / GP:
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       nx_off = 0;
       ++nx_blk;
     }
-    const uint32_t dst = lds_offset(scratch[wave]) + bsel * GE::kTileBuf;
+    const uint32_t dst = lds_offset(stage[wave]) + bsel * GE::kTileBuf;
     wait_lds_reads();  // earlier reads of this buffer (or the query plane) have executed
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
@@ -971,7 +972,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     m_run = mm;
   }
   if (col < G) {
-    float *dst = part_base + static_cast<int64_t>(col) * p.splits_total * pstride;
+    float *dst = part_base + static_cast<int64_t>(col) * pstride;
     if (kq == 0) {
       dst[0] = m_run;
       dst[1] = l_lane;
@@ -1043,7 +1044,8 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
   const int n = min(max(min(max(p.ring_lens[b], 0), p.ring_cap) - c0, 0), kRingChunk);
   const int pstride = partial_stride(D);
   const int64_t part0 = static_cast<int64_t>(b) * p.num_q_heads + h * G;
-  const int slot = p.max_splits + chunk;
+  // this chunk's partial row (G query heads)
+  float *prow = p.ring_partials + ((static_cast<int64_t>(b) * p.num_kv_heads + h) * p.ring_chunks + chunk) * G * pstride;
 
   // A chunk that no query head sees (past the ring's length, or past every
   // row's causal limit in a prefill chunk) gets the empty partial (m = -inf,
@@ -1053,7 +1055,7 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
   if (!__syncthreads_or(live)) {
     for (int e = tid; e < G * pstride; e += kRingThreads) {
       const int g = e / pstride, j = e - g * pstride;
-      p.partials[((part0 + g) * p.splits_total + slot) * pstride + j] = j == 0 ? -INFINITY : 0.0f;
+      prow[static_cast<int64_t>(g) * pstride + j] = j == 0 ? -INFINITY : 0.0f;
     }
     return;
   }
@@ -1145,7 +1147,7 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
     if (lane < kRingChunk) p_s[g][lane] = pt;
     const float l = wave_sum(pt);
     if (lane == 0) {
-      float *dst = p.partials + ((part0 + g) * p.splits_total + slot) * pstride;
+      float *dst = prow + static_cast<int64_t>(g) * pstride;
       dst[0] = m;
       dst[1] = l;
     }
@@ -1183,7 +1185,7 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
 #pragma unroll
     for (int a = 0; a < kAcc; ++a) {
       const int g = grp + a * kHeadGroups;
-      if (g < G) p.partials[((part0 + g) * p.splits_total + slot) * pstride + 4 + col] = acc[a];
+      if (g < G) prow[static_cast<int64_t>(g) * pstride + 4 + col] = acc[a];
     }
   }
 }
@@ -1206,21 +1208,29 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
   const int col = tid % kCols;
   const int r = tid / kCols;
   const int G = p.num_q_heads / p.num_kv_heads;
+  const int h = hq / G;
+  const int g = hq - h * G;
   const int ps = partial_stride(D);
+  const int64_t seg = static_cast<int64_t>(b) * p.num_kv_heads + h;
   int nslots = 0;
-  if (p.max_splits > 0) {
-    // the split kernel's work division (header written before this launch)
+  int64_t row0 = 0;
+  if (p.max_seq_len > 0) {
+    // the split kernel's work division (header written before this launch):
+    // waves w0..w1 covered segment (b, h) and wrote rows w0 + seg .. w1 + seg
     const long long total = reinterpret_cast<const long long *>(p.plan)[0];
     const int active = p.plan[2];
     const int pb = p.plan[4 + b];
     const int nb = p.plan[4 + b + 1] - pb;
     if (nb > 0) {
-      const long long s0 = static_cast<long long>(pb) * p.num_kv_heads + static_cast<long long>(hq / G) * nb;
-      nslots = first_wave(s0 + nb - 1, total, active) - first_wave(s0, total, active) + 1;
+      const long long s0 = static_cast<long long>(pb) * p.num_kv_heads + static_cast<long long>(h) * nb;
+      const int w0 = first_wave(s0, total, active);
+      nslots = first_wave(s0 + nb - 1, total, active) - w0 + 1;
+      row0 = w0 + seg;
     }
   }
-  const int n = nslots + (p.splits_total - p.max_splits);  // + ring chunks
-  const float *part = p.partials + (static_cast<int64_t>(b) * p.num_q_heads + hq) * p.splits_total * ps;
+  const int n = nslots + p.ring_chunks;
+  const float *part = p.partials + (row0 * G + g) * ps;                       // row stride G ps
+  const float *ring_part = p.ring_partials + (seg * p.ring_chunks * G + g) * ps;
   float m = -INFINITY, l = 0.0f;
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (r < R) {
@@ -1234,7 +1244,8 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
         ls[i] = 0.0f;
         as[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
         if (s < n) {
-          const float *e = part + static_cast<int64_t>(s < nslots ? s : p.max_splits + (s - nslots)) * ps;
+          const float *e = s < nslots ? part + static_cast<int64_t>(s) * G * ps
+                                      : ring_part + static_cast<int64_t>(s - nslots) * G * ps;
           ms[i] = e[0];
           ls[i] = e[1];
           as[i] = reinterpret_cast<const float4_t *>(e + kPartStride_pad)[col];
@@ -1303,26 +1314,36 @@ int resident_workgroups(const void *kernel, size_t dyn_lds) {
   return n;
 }
 
+// Workgroups of one split launch: enough waves for the largest possible
+// context, capped at what fits on the device at once. 0 when no split
+// kernel runs (no compressed tokens); < 0 on a HIP error.
+template <int D, int KB, int VB, int NB>
+int split_grid(const DecodeParams &p) {
+  if (p.batch == 0 || p.max_seq_len <= 0) return 0;
+  const size_t dyn = static_cast<size_t>(p.batch + 1) * sizeof(int32_t);
+  const void *kern = reinterpret_cast<const void *>(&decode_split_kernel<D, KB, VB, NB>);
+  const int resident = resident_workgroups(kern, dyn);
+  if (resident < 0) return -1;
+  const long long worst_tiles = static_cast<long long>(p.batch) * p.num_kv_heads * ((p.max_seq_len + kTile - 1) / kTile);
+  const long long need = (work_waves(worst_tiles, 1 << 30, p.split_tokens) + kWaves - 1) / kWaves;
+  return static_cast<int>(std::max(1LL, std::min<long long>(need, resident)));
+}
+
 template <int D, int KB, int VB, int NB>
 int launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s) {
+  const int grid = split_grid<D, KB, VB, NB>(p);
+  if (grid < 0) return hipErrorInvalidValue;
   if (p.batch == 0) return hipSuccess;
   const int qd = static_cast<int>(q_dtype);
-  if (p.max_splits > 0) {
+  if (grid > 0) {
     const size_t dyn = static_cast<size_t>(p.batch + 1) * sizeof(int32_t);
-    const void *kern = reinterpret_cast<const void *>(&decode_split_kernel<D, KB, VB, NB>);
-    const int resident = resident_workgroups(kern, dyn);
-    if (resident < 0) return hipErrorInvalidValue;
-    // enough waves for the largest possible context, capped at what fits
-    const long long worst_tiles = static_cast<long long>(p.batch) * p.num_kv_heads * ((p.max_seq_len + kTile - 1) / kTile);
-    const long long need = (work_waves(worst_tiles, 1 << 30, p.split_tokens) + kWaves - 1) / kWaves;
-    const int grid = static_cast<int>(std::max(1LL, std::min<long long>(need, resident)));
     hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, NB>), dim3(grid), dim3(64 * kWaves), dyn, s, p, qd);
     const int err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (p.ring_cap > 0) {
-    const int chunks = (p.ring_cap + kRingChunk - 1) / kRingChunk;
-    hipLaunchKernelGGL((decode_ring_kernel<D>), dim3(p.num_kv_heads, p.batch, chunks), dim3(kRingThreads), 0, s, p, qd);
+    hipLaunchKernelGGL((decode_ring_kernel<D>), dim3(p.num_kv_heads, p.batch, p.ring_chunks), dim3(kRingThreads), 0, s,
+                       p, qd);
     const int err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

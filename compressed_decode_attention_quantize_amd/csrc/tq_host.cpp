@@ -145,15 +145,23 @@ void layer_sign_mask(const tq_config &cfg, int layer_idx, uint32_t words[4]) {
   }
 }
 
+namespace {
+
+void plan_offsets(const tq_config &cfg, int batch, int num_q_heads, SplitPlan *plan) {
+  const size_t row = static_cast<size_t>(cfg.head_dim + 4) * sizeof(float);  // [m, l, -, -, acc[D]]
+  plan->header_bytes = ((16 + 4 * (static_cast<size_t>(batch) + 1) + 255) / 256) * 256;
+  plan->ring_offset = plan->header_bytes + ((static_cast<size_t>(plan->head_rows) * row + 255) / 256) * 256;
+  plan->workspace_bytes = plan->ring_offset + static_cast<size_t>(batch) * num_q_heads * plan->ring_chunks * row;
+}
+
+}  // namespace
+
 tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_seq_len,
                       int ring_cap, int split_tokens, SplitPlan *plan) {
   if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || ring_cap < 0)
     return fail(TQ_ERR_INVALID_ARG, "decode plan: negative batch/max_seq_len/ring_cap or num_q_heads <= 0");
   if (split_tokens < 0 || split_tokens % 16 != 0)
     return fail(TQ_ERR_INVALID_ARG, "split_tokens must be 0 (auto) or a positive multiple of 16");
-  // A wave covers at least min_tokens tokens (except the last wave of a
-  // short batch), so a (sequence, KV head) spans at most
-  // ceil(len / min_tokens) + 1 waves: one partial slot each.
   // The automatic range: FP8-key decode streams bytes with little compute
   // per tile, and measures fastest with ~2 waves per SIMD on 512-token
   // ranges (fewer range start-ups and partials); the MSE-key decode is
@@ -161,11 +169,22 @@ tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_
   const int min_tokens = split_tokens > 0 ? split_tokens : (cfg.key_fp8 ? kMinTokensPerWaveFp8 : kMinTokensPerWave);
   plan->split_tokens = min_tokens;
   plan->max_splits = max_seq_len > 0 ? ceil_div_i(max_seq_len, min_tokens) + 1 : 0;
-  plan->splits_total = plan->max_splits + (ring_cap + kRingChunk - 1) / kRingChunk;
-  plan->header_bytes = ((16 + 4 * (static_cast<size_t>(batch) + 1) + 255) / 256) * 256;
-  plan->workspace_bytes = plan->header_bytes + static_cast<size_t>(batch) * num_q_heads *
-                                                   std::max(plan->splits_total, 1) * (cfg.head_dim + 4) *
-                                                   sizeof(float);  // rows [m, l, -, -, acc[D]]
+  plan->ring_chunks = (ring_cap + kRingChunk - 1) / kRingChunk;
+  // Compressed partials: wave w writes row w + s for every (sequence, KV
+  // head) segment s it covers, so rows < active waves + segments. The waves
+  // activated are at most max(1, tiles / (min_tokens / 16)) with tiles <=
+  // batch * Hkv * ceil(max_seq_len / 16); in rows of one query head that is
+  // at most max(Hq, batch * Hq * tiles per sequence / tiles per wave)
+  // + batch * Hq, whatever the number of KV heads.
+  if (max_seq_len > 0) {
+    const long long tiles = (static_cast<long long>(max_seq_len) + 15) / 16;
+    const long long per_wave = min_tokens / 16;
+    const long long wave_rows = (static_cast<long long>(batch) * num_q_heads * tiles + per_wave - 1) / per_wave;
+    plan->head_rows = std::max<long long>(num_q_heads, wave_rows) + static_cast<long long>(batch) * num_q_heads;
+  } else {
+    plan->head_rows = 0;
+  }
+  plan_offsets(cfg, batch, num_q_heads, plan);
   return TQ_OK;
 }
 
@@ -325,7 +344,7 @@ TQ_EXPORT tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, in
   st = plan_decode(*cfg, batch, num_q_heads, max_seq_len, ring_cap, split_tokens, &plan);
   if (st != TQ_OK) return st;
   *bytes_out = plan.workspace_bytes;
-  if (num_splits_out) *num_splits_out = plan.splits_total;
+  if (num_splits_out) *num_splits_out = plan.max_splits + plan.ring_chunks;
   return TQ_OK;
 }
 

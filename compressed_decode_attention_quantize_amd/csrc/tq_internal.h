@@ -77,7 +77,12 @@ struct DecodeParams {
   const uint16_t *ring_k;  // bf16 bits
   const uint16_t *ring_v;
   const int32_t *ring_lens;
-  float *partials;         // [batch][Hq][splits_total][D + 4]: m, l, pad, pad, acc[D]
+  // Partials, rows of G query heads x [m, l, pad, pad, acc[D]] fp32:
+  //  compressed tokens: wave w's partial of segment s = b * Hkv + h (the
+  //  waves' ranges are consecutive, so w + s is unique) is row w + s;
+  //  ring chunks: row (s * ring_chunks + chunk) of ring_partials.
+  float *partials;
+  float *ring_partials;
   float *out;
   int64_t num_blocks;
   int32_t batch;
@@ -88,8 +93,7 @@ struct DecodeParams {
   int32_t max_seq_len;
   int32_t ring_cap;
   int32_t split_tokens;    // minimum tokens per wave (multiple of 16)
-  int32_t max_splits;      // partial slots per (sequence, q head) for compressed tokens
-  int32_t splits_total;    // max_splits + ceil(ring_cap / kRingChunk): slots max_splits.. are the ring's
+  int32_t ring_chunks;     // ceil(ring_cap / kRingChunk)
   int32_t *plan;           // workspace header: [total tiles (int64), active waves, -, tile prefix[batch + 1]]
   int32_t slot_bytes;
   int32_t key_bytes;
@@ -150,11 +154,14 @@ int launch_decode(const tq_config &cfg, tq_dtype q_dtype, const DecodeParams &p,
 // Split plan shared by tq_decode_workspace_size and tq_decode_attention.
 struct SplitPlan {
   int32_t split_tokens;   // as given (0 = 256 tokens per wave at least)
-  int32_t max_splits;     // partial slots per (sequence, q head) for compressed tokens
-  int32_t splits_total;   // max_splits + one slot per kRingChunk ring tokens
+  int32_t max_splits;     // partials per (sequence, KV head) at most: ceil(max_seq_len / split_tokens) + 1
+  int32_t ring_chunks;    // one partial per kRingChunk ring tokens
+  int64_t head_rows;      // compressed-token partial rows of one query head each
   size_t header_bytes;    // work-division header (16 + 4 (batch + 1), rounded to 256)
-  size_t workspace_bytes; // header + partials
+  size_t ring_offset;     // byte offset of the ring partials
+  size_t workspace_bytes; // header + compressed partials + ring partials
 };
+
 constexpr int kMinTokensPerWave = 256;     // default range of a decode wave (MSE keys)
 constexpr int kMinTokensPerWaveFp8 = 512;  // FP8 keys: fewer, longer ranges
 constexpr int kRingChunk = 32;  // ring tokens per partial slot

@@ -288,12 +288,14 @@ tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx,
  * gives every resident wave an equal contiguous range of them, of at least
  * split_tokens tokens (a positive multiple of 16; 0 means 512 with FP8 keys
  * and 256 otherwise), so the work is balanced whatever the mix of lengths.
- * The workspace holds a header
- * (16 + 4 (batch + 1) bytes, rounded up to 256) and one fp32 partial
- * (max, sum, acc[head_dim]) per (sequence, query head, slot) with
- * ceil(max_seq_len / min tokens) + 1 slots, plus one per 32 ring tokens
- * (ceil(ring_cap / 32)). num_splits_out (nullable) receives the slots per
- * sequence.
+ * The workspace holds a header (16 + 4 (batch + 1) bytes, rounded up to
+ * 256), then the fp32 partials (max, sum, acc[head_dim]) of the compressed
+ * tokens: a wave writes one per query head of every (sequence, KV head) it
+ * covers, at most max(Hq, batch Hq ceil(max_seq_len / 16) / (split_tokens /
+ * 16)) + batch Hq of them (rounded up to 256 bytes), then one per (sequence,
+ * query head) and 32 ring tokens (ceil(ring_cap / 32) each). num_splits_out
+ * (nullable) receives the partials one (sequence, query head) can have:
+ * ceil(max_seq_len / split_tokens) + 1 + ceil(ring_cap / 32).
  */
 tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, int num_q_heads,
                                    int max_seq_len, int ring_cap, int split_tokens,

@@ -188,24 +188,28 @@ def test_decode_argument_errors_before_launch():
 
 def test_workspace_size_and_plan():
     c = tq.config_from_preset("turboquant_k8v4", 128)
-    # a wave covers >= 256 tokens, so a sequence spans <= 8192/256 + 1 waves
+    row = 132 * 4                                   # [m, l, -, -, acc[128]] fp32
+    # 16 sequences x 8192 tokens, ranges of >= 256 tokens: at most
+    # 16 * 32 * 512 / 16 wave rows + 16 * 32 segment rows of one query head
     b, n = tq.decode_workspace_size(c, 16, 32, 8192, 0, 256)
-    assert n == 33 and b == 256 + 16 * 32 * 33 * 132 * 4
-    # one partial slot per 32 ring tokens
+    assert n == 33 and b == 256 + (16384 + 512) * row
+    # one ring partial per (sequence, query head) and 32 ring tokens
     b, n = tq.decode_workspace_size(c, 16, 32, 8192, 128, 256)
-    assert n == 37
+    assert n == 37 and b == 256 + (16384 + 512) * row + 16 * 32 * 4 * row
     _, n = tq.decode_workspace_size(c, 16, 32, 8192, 100, 256)
     assert n == 37
     b, n = tq.decode_workspace_size(c, 4, 8, 0, 0, 0)
-    assert n == 0 and b == 256 + 4 * 8 * 1 * 132 * 4
+    assert n == 0 and b == 256
     # automatic ranges: 512 tokens with FP8 keys, 256 with MSE keys
     _, n_auto = tq.decode_workspace_size(c, 16, 32, 8192)
     assert n_auto == 17
     _, n_auto = tq.decode_workspace_size(tq.config_from_preset("turboquant_4bit_nc", 128), 16, 32, 8192)
     assert n_auto == 33
-    # the header grows with the batch (tile prefix per sequence)
+    # the header grows with the batch (tile prefix per sequence); 100 tokens
+    # are 7 tiles, 512-token ranges 32 tiles: ceil(100 * 8 * 7 / 32) = 175
+    # wave rows + 800 segment rows, the block rounded up to 256 bytes
     b, _ = tq.decode_workspace_size(c, 100, 8, 100, 0, 0)
-    assert b == 512 + 100 * 8 * 2 * 132 * 4
+    assert b == 512 + -(-(975 * row) // 256) * 256
 
 
 @pytest.mark.parametrize("num_layers", [0, 1, 2, 3, 4, 5, 10, 28, 32, 61])
