@@ -61,7 +61,7 @@ EXPORTED = ["tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_bo
             "tq_attn_page_size_1_token", "tq_slot_size", "tq_page_size",
             "tq_layer_signs", "tq_quantize_append", "tq_ring_flush", "tq_ring_append", "tq_decode_workspace_size",
             "tq_prefill_workspace_size", "tq_prefill_attention",
-            "tq_decode_attention", "tq_dequant", "tq_last_error", "tq_version"]
+            "tq_decode_attention", "tq_decode_attention_no_alloc", "tq_dequant", "tq_last_error", "tq_version"]
 
 
 class Config(ctypes.Structure):
@@ -125,10 +125,14 @@ _lib.tq_decode_attention.argtypes = [_CP, ctypes.c_int, _P, ctypes.c_int, ctypes
                                      ctypes.c_int, _P, _i64, ctypes.c_int, _P, ctypes.c_int, _P,
                                      ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _sz,
                                      ctypes.c_int, _P]
+_lib.tq_decode_attention_no_alloc.argtypes = [_CP, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, _P, _i64, ctypes.c_int, _P, ctypes.c_int, _P,
+                                              ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P,
+                                              ctypes.c_int, _P]
 _lib.tq_dequant.argtypes = [_CP, ctypes.c_int, _P, _i64, ctypes.c_int, ctypes.c_int, _P, _i64, _P, _P, _P]
 for _name in ("tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_layer_signs", "tq_quantize_append",
               "tq_ring_flush", "tq_ring_append", "tq_prefill_workspace_size", "tq_prefill_attention",
-              "tq_decode_workspace_size", "tq_decode_attention", "tq_dequant"):
+              "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_attention_no_alloc", "tq_dequant"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.tq_last_error.restype = ctypes.c_char_p
 _lib.tq_version.restype = ctypes.c_char_p
@@ -409,6 +413,28 @@ def decode_attention(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_
                                     block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(),
                                     max_seq_len, rk, rv, rl, ring_cap, float(softmax_scale), out.data_ptr(),
                                     workspace.data_ptr(), workspace.numel(), split_tokens, s))
+    return out
+
+
+def decode_attention_no_alloc(cfg: Config, layer_idx: int, q, kv_pool, block_tables, seq_lens, max_seq_len: int,
+                              out, ring_k=None, ring_v=None, ring_lens=None, softmax_scale: float = 0.0,
+                              split_tokens: int = 0, stream=None):
+    """decode_attention through tq_decode_attention_no_alloc: the caller
+    passes `out` (float32 [B, Hq, D]); the library's per-device static
+    scratch takes the workspace's place, so nothing is allocated. Calls that
+    overlap on one device race."""
+    torch = _torch()
+    bsz, hq, hkv, d, ring_cap, rk, rv, rl = _decode_args(cfg, q, kv_pool, block_tables, seq_lens,
+                                                         ring_k, ring_v, ring_lens)
+    _dev(out, "out", torch.float32)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 like q")
+    s = stream if stream is not None else _stream_ptr(q)
+    _check(_lib.tq_decode_attention_no_alloc(ctypes.byref(cfg), layer_idx, q.data_ptr(), _dtype_code(q), bsz, hq,
+                                             hkv, kv_pool.data_ptr(), kv_pool.shape[0], kv_pool.shape[2],
+                                             block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(),
+                                             max_seq_len, rk, rv, rl, ring_cap, float(softmax_scale),
+                                             out.data_ptr(), split_tokens, s))
     return out
 
 

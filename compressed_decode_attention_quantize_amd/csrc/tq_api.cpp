@@ -426,3 +426,37 @@ TQ_EXPORT tq_status tq_decode_attention(const tq_config *cfg, int layer_idx, con
   if (err != hipSuccess) return hip_fail("tq_decode_attention launch", err);
   return TQ_OK;
 }
+
+TQ_EXPORT tq_status tq_decode_attention_no_alloc(const tq_config *cfg, int layer_idx, const void *q, tq_dtype q_dtype,
+                                                 int batch, int num_q_heads, int num_kv_heads, const uint8_t *kv_pool,
+                                                 int64_t num_blocks, int block_size, const int32_t *block_tables,
+                                                 int max_blocks_per_seq, const int32_t *seq_lens, int max_seq_len,
+                                                 const void *ring_k, const void *ring_v, const int32_t *ring_lens,
+                                                 int ring_cap, float softmax_scale, float *out, int split_tokens,
+                                                 void *stream) {
+  DecodeParams p;
+  SplitPlan plan;
+  bool run = false;
+  tq_status st = decode_setup("tq_decode_attention_no_alloc", cfg, layer_idx, q, q_dtype, batch, num_q_heads,
+                              num_kv_heads, kv_pool, num_blocks, block_size, block_tables, max_blocks_per_seq,
+                              seq_lens, max_seq_len, ring_k, ring_v, ring_lens, ring_cap, softmax_scale, out,
+                              split_tokens, &p, &plan, &run);
+  if (st != TQ_OK || !run) return st;
+  // the partials this launch can write: its split waves + one row per segment
+  const long long waves = decode_launch_waves(*cfg, p);
+  if (waves < 0) return hip_fail("tq_decode_attention_no_alloc occupancy query", hipErrorInvalidValue);
+  plan_for_launch(*cfg, batch, num_q_heads, num_kv_heads, waves, &plan);
+  void *ws = nullptr;
+  size_t cap = 0;
+  const int e = static_scratch(&ws, &cap);
+  if (e != hipSuccess) return hip_fail("tq_decode_attention_no_alloc scratch address", e);
+  if (plan.workspace_bytes > cap)
+    return fail(TQ_ERR_WORKSPACE, "tq_decode_attention_no_alloc: this call needs " +
+                                      std::to_string(plan.workspace_bytes) + " bytes of scratch, more than the " +
+                                      std::to_string(cap) + " the library holds per device; use tq_decode_attention "
+                                      "with a caller workspace");
+  bind_workspace(p, plan, ws);
+  const int err = launch_decode(*cfg, q_dtype, p, stream);
+  if (err != hipSuccess) return hip_fail("tq_decode_attention_no_alloc launch", err);
+  return TQ_OK;
+}

@@ -1329,10 +1329,12 @@ int split_grid(const DecodeParams &p) {
   return static_cast<int>(std::max(1LL, std::min<long long>(need, resident)));
 }
 
+// launch = false: only the split grid, as waves (for sizing the partials).
 template <int D, int KB, int VB, int NB>
-int launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s) {
+long long launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s, bool launch) {
   const int grid = split_grid<D, KB, VB, NB>(p);
-  if (grid < 0) return hipErrorInvalidValue;
+  if (grid < 0) return -1;
+  if (!launch) return static_cast<long long>(grid) * kWaves;
   if (p.batch == 0) return hipSuccess;
   const int qd = static_cast<int>(q_dtype);
   if (grid > 0) {
@@ -1352,38 +1354,74 @@ int launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s) {
 }
 
 template <int D, int KB, int VB>
-int dispatch_decode_group(tq_dtype qd, const DecodeParams &p, hipStream_t s) {
+long long dispatch_decode_group(tq_dtype qd, const DecodeParams &p, hipStream_t s, bool launch) {
   const int G = p.num_q_heads / p.num_kv_heads;
-  if (G <= 4) return launch_decode_t<D, KB, VB, 4>(qd, p, s);
-  if (G <= 8) return launch_decode_t<D, KB, VB, 2>(qd, p, s);
-  return launch_decode_t<D, KB, VB, 1>(qd, p, s);
+  if (G <= 4) return launch_decode_t<D, KB, VB, 4>(qd, p, s, launch);
+  if (G <= 8) return launch_decode_t<D, KB, VB, 2>(qd, p, s, launch);
+  return launch_decode_t<D, KB, VB, 1>(qd, p, s, launch);
 }
 
 template <int D>
-int dispatch_decode_bits(const tq_config &c, tq_dtype qd, const DecodeParams &p, hipStream_t s) {
+long long dispatch_decode_bits(const tq_config &c, tq_dtype qd, const DecodeParams &p, hipStream_t s, bool launch) {
   const int kb = c.key_quant_bits, vb = c.value_quant_bits;
-  if (kb == 3 && vb == 2) return dispatch_decode_group<D, 3, 2>(qd, p, s);
-  if (kb == 4 && vb == 2) return dispatch_decode_group<D, 4, 2>(qd, p, s);
-  if (kb == 8 && vb == 2) return dispatch_decode_group<D, 8, 2>(qd, p, s);
-  if (kb == 3 && vb == 3) return dispatch_decode_group<D, 3, 3>(qd, p, s);
-  if (kb == 3 && vb == 4) return dispatch_decode_group<D, 3, 4>(qd, p, s);
-  if (kb == 4 && vb == 3) return dispatch_decode_group<D, 4, 3>(qd, p, s);
-  if (kb == 4 && vb == 4) return dispatch_decode_group<D, 4, 4>(qd, p, s);
-  if (kb == 8 && vb == 3) return dispatch_decode_group<D, 8, 3>(qd, p, s);
-  if (kb == 8 && vb == 4) return dispatch_decode_group<D, 8, 4>(qd, p, s);
-  return hipErrorInvalidValue;
+  if (kb == 3 && vb == 2) return dispatch_decode_group<D, 3, 2>(qd, p, s, launch);
+  if (kb == 4 && vb == 2) return dispatch_decode_group<D, 4, 2>(qd, p, s, launch);
+  if (kb == 8 && vb == 2) return dispatch_decode_group<D, 8, 2>(qd, p, s, launch);
+  if (kb == 3 && vb == 3) return dispatch_decode_group<D, 3, 3>(qd, p, s, launch);
+  if (kb == 3 && vb == 4) return dispatch_decode_group<D, 3, 4>(qd, p, s, launch);
+  if (kb == 4 && vb == 3) return dispatch_decode_group<D, 4, 3>(qd, p, s, launch);
+  if (kb == 4 && vb == 4) return dispatch_decode_group<D, 4, 4>(qd, p, s, launch);
+  if (kb == 8 && vb == 3) return dispatch_decode_group<D, 8, 3>(qd, p, s, launch);
+  if (kb == 8 && vb == 4) return dispatch_decode_group<D, 8, 4>(qd, p, s, launch);
+  return launch ? hipErrorInvalidValue : -1;
+}
+
+long long dispatch_decode(const tq_config &c, tq_dtype q_dtype, const DecodeParams &p, hipStream_t s, bool launch) {
+  switch (c.head_dim) {
+    case 64: return dispatch_decode_bits<64>(c, q_dtype, p, s, launch);
+    case 96: return dispatch_decode_bits<96>(c, q_dtype, p, s, launch);
+    case 128: return dispatch_decode_bits<128>(c, q_dtype, p, s, launch);
+  }
+  return launch ? hipErrorInvalidValue : -1;
 }
 
 }  // namespace
 
-int launch_decode(const tq_config &c, tq_dtype q_dtype, const DecodeParams &p, void *stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (c.head_dim) {
-    case 64: return dispatch_decode_bits<64>(c, q_dtype, p, s);
-    case 96: return dispatch_decode_bits<96>(c, q_dtype, p, s);
-    case 128: return dispatch_decode_bits<128>(c, q_dtype, p, s);
+// Scratch of the no-allocation decode entry point: the work-division header
+// and the partials live here instead of in caller memory. Each device that
+// loads the library holds one copy until the process ends; every call on a
+// device shares it, so calls that overlap on one device race.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+int static_scratch(void **ptr, size_t *bytes) {
+  // The array's name in host code is a host-side stand-in, not a device
+  // address: the device address is looked up once per device, with that
+  // device current, and kept.
+  static std::mutex mu;
+  static std::map<int, void *> addr;
+  int dev = 0;
+  int err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    it = addr.emplace(dev, p).first;
   }
-  return hipErrorInvalidValue;
+  *ptr = it->second;
+  *bytes = kStaticScratchBytes;
+  return hipSuccess;
+}
+
+long long decode_launch_waves(const tq_config &c, const DecodeParams &p) {
+  return dispatch_decode(c, TQ_BF16, p, nullptr, false);
+}
+
+int launch_decode(const tq_config &c, tq_dtype q_dtype, const DecodeParams &p, void *stream) {
+  return static_cast<int>(dispatch_decode(c, q_dtype, p, static_cast<hipStream_t>(stream), true));
 }
 
 }  // namespace tq

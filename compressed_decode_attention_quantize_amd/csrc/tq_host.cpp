@@ -188,6 +188,16 @@ tq_status plan_decode(const tq_config &cfg, int batch, int num_q_heads, int max_
   return TQ_OK;
 }
 
+void plan_for_launch(const tq_config &cfg, int batch, int num_q_heads, int num_kv_heads, long long waves,
+                     SplitPlan *plan) {
+  if (plan->head_rows > 0) {
+    const long long g = num_q_heads / num_kv_heads;
+    const long long rows = (std::max(waves, 1LL) + static_cast<long long>(batch) * num_kv_heads) * g;
+    plan->head_rows = std::min<long long>(plan->head_rows, rows);
+  }
+  plan_offsets(cfg, batch, num_q_heads, plan);
+}
+
 }  // namespace tq
 
 using namespace tq;

@@ -150,6 +150,12 @@ int launch_ring_commit(int32_t *ring_lens, int32_t *seq_lens, int batch, int rin
 int launch_ring_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *ring_k, uint16_t *ring_v,
                        int32_t *ring_lens, int batch, int num_kv_heads, int head_dim, int ring_cap, void *stream);
 int launch_decode(const tq_config &cfg, tq_dtype q_dtype, const DecodeParams &p, void *stream);
+// Waves the decode split kernel launch for these parameters uses on the
+// current device (0 when none is launched); < 0 on a HIP error.
+long long decode_launch_waves(const tq_config &cfg, const DecodeParams &p);
+// The per-device static scratch of the no-allocation decode: its device
+// address on the current device (looked up once per device) and its size.
+int static_scratch(void **ptr, size_t *bytes);
 
 // Split plan shared by tq_decode_workspace_size and tq_decode_attention.
 struct SplitPlan {
@@ -161,7 +167,10 @@ struct SplitPlan {
   size_t ring_offset;     // byte offset of the ring partials
   size_t workspace_bytes; // header + compressed partials + ring partials
 };
-
+// Shrinks a plan to a known split launch of `waves` waves over num_kv_heads
+// KV heads: at most (waves + batch * num_kv_heads) rows of G heads.
+void plan_for_launch(const tq_config &cfg, int batch, int num_q_heads, int num_kv_heads, long long waves,
+                     SplitPlan *plan);
 constexpr int kMinTokensPerWave = 256;     // default range of a decode wave (MSE keys)
 constexpr int kMinTokensPerWaveFp8 = 512;  // FP8 keys: fewer, longer ranges
 constexpr int kRingChunk = 32;  // ring tokens per partial slot

@@ -346,6 +346,34 @@ tq_status tq_decode_attention(const tq_config *cfg, int layer_idx,
                               int split_tokens, void *stream);
 
 /*
+ * tq_decode_attention without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments, meaning and result as tq_decode_attention.
+ *
+ * The header and partials go to a static scratch array of 32 MiB that the
+ * library holds on every device it runs on until the process ends (its
+ * device address is looked up once per device, on the first call there).
+ * A call whose partials need more (its split waves plus batch *
+ * num_kv_heads, times num_q_heads / num_kv_heads rows of head_dim + 4
+ * floats, plus the ring partials) returns TQ_ERR_WORKSPACE before anything
+ * is enqueued. All calls on one device share the array: calls that overlap
+ * on one device (concurrent streams, or host threads) race and give wrong
+ * results; serialise them. Nothing in the array needs clearing between
+ * calls (every partial a call reads is written in that call).
+ */
+tq_status tq_decode_attention_no_alloc(const tq_config *cfg, int layer_idx,
+                                       const void *q, tq_dtype q_dtype,
+                                       int batch, int num_q_heads, int num_kv_heads,
+                                       const uint8_t *kv_pool, int64_t num_blocks, int block_size,
+                                       const int32_t *block_tables, int max_blocks_per_seq,
+                                       const int32_t *seq_lens, int max_seq_len,
+                                       const void *ring_k, const void *ring_v,
+                                       const int32_t *ring_lens, int ring_cap,
+                                       float softmax_scale, float *out,
+                                       int split_tokens, void *stream);
+
+/*
  * Dequantize slots back to the original basis ([API] docstring: centroids,
  * re-normalized under norm correction, then the inverse rotation; values
  * scale' * code + zero'), fp32 with the oracle's fixed operation order:
