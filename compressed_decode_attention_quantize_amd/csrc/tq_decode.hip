@@ -104,16 +104,18 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)(p)));
 }
 
-// Direct HBM -> LDS load of 16 bytes per lane: lane l's bytes land at LDS
-// offset lds_base + 16 l (lds_base is wave-uniform). Issued as inline asm so
-// the compiler does not hold later LDS reads of other buffers behind it;
-// callers wait for it with wait_vmcnt before reading the destination.
-__device__ __forceinline__ void load_lds_16(const void *gaddr, uint32_t lds_base) {
+// Direct HBM -> LDS load of 16 bytes per lane from a wave-uniform base in
+// SGPRs: lane l's 16 bytes at sbase + voff (voff a per-lane VGPR offset,
+// no per-lane 64-bit address arithmetic) land at LDS offset lds_base + 16 l
+// (lds_base wave-uniform). Issued as inline asm so the compiler does not
+// hold later LDS reads of other buffers behind it; callers wait for it with
+// wait_vmcnt before reading the destination.
+__device__ __forceinline__ void load_lds_16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, off"
+      "global_load_lds_dwordx4 %1, %2"
       :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(gaddr)
+      : "s"(lds_base), "v"(voff), "s"(sbase)
       : "memory", "m0");
 }
 
@@ -346,6 +348,28 @@ __device__ __forceinline__ void key_operand(const uint32_t *words, uint32_t off,
       kf[m] = __builtin_bit_cast(half8_t, v);
     }
   }
+}
+
+// Lane l takes a if bit l of the lane mask m is set, else b: one
+// v_cndmask_b32, kept from the compiler, which otherwise may turn a
+// lane-dependent select whose arms differ in cost into a divergent branch.
+// Masks of loop-invariant conditions are computed once, outside the loops.
+// Never pass an MFMA result straight in: the compiler inserts no MFMA
+// hazard wait states before inline asm.
+__device__ __forceinline__ float mask_select(uint64_t m, float a, float b) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
+  return r;
+}
+__device__ __forceinline__ uint32_t mask_select(uint64_t m, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
+  return r;
+}
+__device__ __forceinline__ uint64_t lane_mask(bool c) { return __builtin_amdgcn_ballot_w64(c); }
+// Lanes whose column (lane % 16) is below n, for 0 <= n <= 16.
+__device__ __forceinline__ uint64_t column_mask(int n) {
+  return ((1ull << n) - 1ull) * 0x0001000100010001ull;
 }
 
 // Hand-off of LDS data between lanes of one wave: lanes write, other lanes
@@ -633,6 +657,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   for (int c = 0; c < 8; ++c) acc[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_lane = 0.0f, z_lane = 0.0f;
   const int my_tile = col / GP;  // column group of this lane's column
+  // lane masks of loop-invariant conditions
+  uint64_t m_grp[NB];  // lanes of column group j
+#pragma unroll
+  for (int j = 0; j < NB; ++j) m_grp[j] = lane_mask(my_tile == j);
+  const uint64_t m_kq0 = lane_mask(kq == 0), m_kq1 = lane_mask(kq == 1), m_kq3 = lane_mask(kq == 3);
+  // the Gram diagonal of token col sits in register col - 4 kq of lane row
+  // kq: one-hot weights pick it with exact multiply-adds (the Gram entries
+  // are finite). Ordinary arithmetic on purpose: an inline-asm select that
+  // reads an MFMA result is invisible to the compiler's MFMA hazard checks
+  // and could read the registers before the MFMA has written them.
+  const int diag_r = col - 4 * kq;
+  const float dsel0 = diag_r == 0 ? 1.0f : 0.0f, dsel1 = diag_r == 1 ? 1.0f : 0.0f;
+  const float dsel2 = diag_r == 2 ? 1.0f : 0.0f, dsel3 = diag_r == 3 ? 1.0f : 0.0f;
 
   // Tiles go HBM -> LDS by direct loads (global_load_lds_dwordx4: lane l of
   // a load instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS window),
@@ -646,6 +683,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   const uint32_t blk_stride = static_cast<uint32_t>(p.num_kv_heads * p.block_size * S);
   const uint8_t *head_base = p.pool + static_cast<int64_t>(h) * p.block_size * S;
   const uint32_t nblk = static_cast<uint32_t>(p.num_blocks < 0x7fffffff ? p.num_blocks : 0x7fffffff);
+  // this wave's staging area in LDS (wave-uniform)
+  const uint32_t stage_base = lds_offset(stage[0]) + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) *
+                                                         (GE::stage_bytes(kBufs) / 4 * 4);
   auto issue = [&](int bsel) {
     const int rel = nx_blk - blk_base;
     int phys;
@@ -666,12 +706,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       nx_off = 0;
       ++nx_blk;
     }
-    const uint32_t dst = lds_offset(stage[wave]) + bsel * GE::kTileBuf;
+    const uint32_t dst = stage_base + bsel * GE::kTileBuf;
     wait_lds_reads();  // earlier reads of this buffer (or the query plane) have executed
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int c = lane + 64 * k;
-      if (c < GE::kTileChunks) load_lds_16(src + 16 * c, dst + 1024 * k);
+      if (c < GE::kTileChunks) load_lds_16s(src, static_cast<uint32_t>(16 * c), dst + 1024 * k);
     }
   };
   issue(0);  // waits for the query plane reads before overwriting it
@@ -682,6 +722,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   int bsel = 0;
   // LDS byte offset of element group col's value codes in token 4kq's slot
   const uint32_t val_off = static_cast<uint32_t>(4 * kq * S + GE::kKeyBytes + VB * col);
+  const uint32_t val_off_rd = static_cast<uint32_t>(4 * kq * S + GE::kKeyBytes + VB * min(col, GE::kGroups - 1));
   for (int mt0 = begin; mt0 < end; mt0 += NT * kTile) {
     uint32_t vraw[kValLds ? 1 : NT][4];
     int tbuf[NT];  // buffer of tile i (wave-uniform)
@@ -711,15 +752,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         // softmax scale (negative marks a masked token), s', z' + c0 s', and
         // 1 in plane 3 (the norm-correction pass overwrites it)
         {
+          // one 4-byte window per lane, the same instructions in every lane:
+          // the norm (plane 0), or the scale and the zero after it
           const uint32_t slot = static_cast<uint32_t>(col * S);
           constexpr uint32_t kScaleOff = GE::kKeyBytes + GE::kValCodeBytes;
-          const float a = f16_bits_to_float(lds_u16(tw, slot + (kq == 0 ? GE::kKeyCodeBytes : kScaleOff)));
-          const float z1 = f16_bits_to_float(lds_u16(tw, slot + kScaleOff + 2));
-          const bool ok = tile_ok && col < ntok;
+          const uint32_t x = lds_bytes<4>(tw, slot + (kq == 0 ? GE::kKeyCodeBytes : kScaleOff)).w[0];
+          const float a = f16_bits_to_float(x & 0xffffu);
+          const float z1 = f16_bits_to_float(x >> 16);
+          const uint64_t ok = tile_ok ? column_mask(ntok) : 0ull;  // live tokens
           const float fb = GE::kMse ? p.scale_log2 * a : p.scale_log2;
-          float val = kq == 0 ? (ok ? fb : -1.0f) : (kq == 1 ? a : fmaf(c0, a, z1));
-          if (kq != 0 && !ok) val = 0.0f;
-          if (kq == 3) val = 1.0f;
+          const float val_k = mask_select(ok, fb, -1.0f);
+          const float val_v = mask_select(ok, mask_select(m_kq1, a, fmaf(c0, a, z1)), 0.0f);
+          float val = mask_select(m_kq0, val_k, val_v);
+          val = mask_select(m_kq3, 1.0f, val);
           tokf[wave][kq][i][col] = val;
         }
 
@@ -744,7 +789,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
           }
         }
         if constexpr (TL == 1) {
-          if (my_tile == i) sraw[0] = sc;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sraw[0][r] = mask_select(m_grp[i], sc[r], sraw[0][r]);
         } else {
           sraw[i] = sc;
         }
@@ -755,9 +801,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
             float4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int m = 0; m < KM; ++m) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], kf[m], gram, 0, 0, 0);
-            const int rr = col - 4 * kq;
-            const float dg = rr == 0 ? gram[0] : rr == 1 ? gram[1] : rr == 2 ? gram[2] : gram[3];
-            tokf[wave][rr >= 0 && rr < 4 ? 3 : 4][i][col] = dg;
+            const float dg = fmaf(gram[3], dsel3, fmaf(gram[2], dsel2, fmaf(gram[1], dsel1, gram[0] * dsel0)));
+            const int plane = static_cast<uint32_t>(diag_r) < 4u ? 3 : 4;
+            tokf[wave][plane][i][col] = dg;
           }
         }
 
@@ -856,9 +902,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         // the tile is still in its buffer: the next load went to the spare one
         const uint32_t *tw = scr + tbuf[i] * (GE::kTileBuf / 4);
         uint32_t vr[4];
+        // every lane reads (lanes past the last element group read group
+        // kGroups - 1, inside the tile, and keep zeros)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vr[r] = col < GE::kGroups ? lds_bytes<VB, GE::kValAligned>(tw, val_off + r * S).w[0] : 0u;
+        for (int r = 0; r < 4; ++r) vr[r] = lds_bytes<VB, GE::kValAligned>(tw, val_off_rd + r * S).w[0];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? vr[r] : 0u;
         VX::prep(vr, pr);  // rows col >= kGroups are padding and never written out
       } else {
         VX::prep(vraw[i], pr);
@@ -887,7 +936,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
           // K rows of tile t: hi weights in group t, lo weights in group
           // (t + NB/2) mod NB, zero elsewhere
           auto pick = [&](int t, int e) -> uint32_t {
-            return my_tile == t ? hw[0][e] : (my_tile == (t + NB / 2) % NB ? lx[e] : 0u);
+            return mask_select(m_grp[t], hw[0][e], mask_select(m_grp[(t + NB / 2) % NB], lx[e], 0u));
           };
           u32x4_t bw;
           bw[0] = pick(i, 0);
@@ -908,15 +957,15 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         }
         u32x4_t bh, bl;
         if constexpr (TL == 1) {
-          const bool m0 = my_tile == i, m1 = my_tile == i + 1;
-          bh[0] = m0 ? hw[0][0] : 0u;
-          bh[1] = m0 ? hw[0][1] : 0u;
-          bh[2] = m1 ? hw[0][0] : 0u;
-          bh[3] = m1 ? hw[0][1] : 0u;
-          bl[0] = m0 ? lw[0][0] : 0u;
-          bl[1] = m0 ? lw[0][1] : 0u;
-          bl[2] = m1 ? lw[0][0] : 0u;
-          bl[3] = m1 ? lw[0][1] : 0u;
+          const uint64_t m0 = m_grp[i], m1 = m_grp[i + 1];
+          bh[0] = mask_select(m0, hw[0][0], 0u);
+          bh[1] = mask_select(m0, hw[0][1], 0u);
+          bh[2] = mask_select(m1, hw[0][0], 0u);
+          bh[3] = mask_select(m1, hw[0][1], 0u);
+          bl[0] = mask_select(m0, lw[0][0], 0u);
+          bl[1] = mask_select(m0, lw[0][1], 0u);
+          bl[2] = mask_select(m1, lw[0][0], 0u);
+          bl[3] = mask_select(m1, lw[0][1], 0u);
         } else {
           bh[0] = hw[0][0];
           bh[1] = hw[0][1];
