@@ -163,6 +163,24 @@ __device__ __forceinline__ Words<(NB + 3) / 4> lds_bytes(const uint32_t *words, 
   return out;
 }
 
+// The NB-byte field (NB <= 4) at byte offset `off` of an LDS word array, in
+// the low bytes of a word, from 16-bit reads: NB = 2 and 4 need an even
+// offset, NB = 3 takes any (two 16-bit reads from the even byte at or below
+// off, then a shift). One register per field, no funnel shift of word
+// pairs, so a tile's fields can all be in flight at once.
+template <int NB>
+__device__ __forceinline__ uint32_t lds_field16(const uint32_t *words, uint32_t off) {
+  static_assert(NB >= 2 && NB <= 4, "field bytes");
+  const uint16_t *h = reinterpret_cast<const uint16_t *>(words);
+  const uint32_t e = off >> 1;
+  if constexpr (NB == 2) {
+    return h[e];
+  } else {
+    const uint32_t y = static_cast<uint32_t>(h[e]) | (static_cast<uint32_t>(h[e + 1]) << 16);
+    return NB == 4 ? y : (y >> (8u * (off & 1u)));
+  }
+}
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -430,7 +448,7 @@ __device__ __forceinline__ uint32_t lds_u16(const uint32_t *words, uint32_t off)
 //          partner group as lo parts, so every group accumulates a mix of
 //          tiles. All groups of a query head therefore share one running
 //          maximum, and the final merge of the groups is a plain sum.
-template <int D, int KB, int VB, int NB>
+template <int D, int KB, int VB, int NB, bool NC>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_kernel(DecodeParams p, int q_dtype) {
   using GE = Geo<D, KB, VB>;
   using VX = ValueExpand<VB>;
@@ -718,7 +736,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
 
   const float c0 = static_cast<float>(VX::kC0);
   const float inv_sigma = 1.0f / p.centroid_scale;
-  const bool nc = GE::kMse && p.norm_correction;
+  constexpr bool nc = GE::kMse && NC;  // norm correction (compile-time: its MFMAs join the tile's schedule)
   int bsel = 0;
   // LDS byte offset of element group col's value codes in token 4kq's slot
   const uint32_t val_off = static_cast<uint32_t>(4 * kq * S + GE::kKeyBytes + VB * col);
@@ -748,15 +766,25 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         tbuf[i] = bsel;
         bsel = nsel;
 
+        // this tile's LDS reads go out together: the per-token scalar window
+        // (the norm for lane row 0, the scale and the zero after it for the
+        // others; the same instructions in every lane) and the key bytes
+        constexpr uint32_t kScaleOff = GE::kKeyBytes + GE::kValCodeBytes;
+        uint32_t x;
+        {
+          // two 16-bit reads into the halves of one register (the fields
+          // are at even offsets of even-sized slots)
+          const uint16_t *h = reinterpret_cast<const uint16_t *>(tw);
+          const uint32_t off = static_cast<uint32_t>(col * S) + (kq == 0 ? GE::kKeyCodeBytes : kScaleOff);
+          x = static_cast<uint32_t>(h[off >> 1]) | (static_cast<uint32_t>(h[(off >> 1) + 1]) << 16);
+        }
+        half8_t kf[KM];
+        key_operand<D, KB, VB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
+
         // per-token scalars of token col, plane kq: the norm times the
         // softmax scale (negative marks a masked token), s', z' + c0 s', and
         // 1 in plane 3 (the norm-correction pass overwrites it)
         {
-          // one 4-byte window per lane, the same instructions in every lane:
-          // the norm (plane 0), or the scale and the zero after it
-          const uint32_t slot = static_cast<uint32_t>(col * S);
-          constexpr uint32_t kScaleOff = GE::kKeyBytes + GE::kValCodeBytes;
-          const uint32_t x = lds_bytes<4>(tw, slot + (kq == 0 ? GE::kKeyCodeBytes : kScaleOff)).w[0];
           const float a = f16_bits_to_float(x & 0xffffu);
           const float z1 = f16_bits_to_float(x >> 16);
           const uint64_t ok = tile_ok ? column_mask(ntok) : 0ull;  // live tokens
@@ -770,8 +798,6 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
 
         // keys -> scores S^T[4kq + r][col]; this lane keeps them if col is in
         // the tile's column group
-        half8_t kf[KM];
-        key_operand<D, KB, VB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
         float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (kFold) {
           // hi parts in group i, lo parts in its partner: one MFMA per K
@@ -795,7 +821,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
           sraw[i] = sc;
         }
         if constexpr (GE::kMse) {
-          if (nc) {
+          if constexpr (nc) {
             // ||c_t||^2 of token t = 4kq + r sits on the Gram diagonal, at
             // lane (kq, col = t), register r
             float4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -905,7 +931,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         // every lane reads (lanes past the last element group read group
         // kGroups - 1, inside the tile, and keep zeros)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vr[r] = lds_bytes<VB, GE::kValAligned>(tw, val_off_rd + r * S).w[0];
+        for (int r = 0; r < 4; ++r) vr[r] = lds_field16<VB>(tw, val_off_rd + r * S);
 #pragma unroll
         for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? vr[r] : 0u;
         VX::prep(vr, pr);  // rows col >= kGroups are padding and never written out
@@ -1366,11 +1392,11 @@ int resident_workgroups(const void *kernel, size_t dyn_lds) {
 // Workgroups of one split launch: enough waves for the largest possible
 // context, capped at what fits on the device at once. 0 when no split
 // kernel runs (no compressed tokens); < 0 on a HIP error.
-template <int D, int KB, int VB, int NB>
+template <int D, int KB, int VB, int NB, bool NC>
 int split_grid(const DecodeParams &p) {
   if (p.batch == 0 || p.max_seq_len <= 0) return 0;
   const size_t dyn = static_cast<size_t>(p.batch + 1) * sizeof(int32_t);
-  const void *kern = reinterpret_cast<const void *>(&decode_split_kernel<D, KB, VB, NB>);
+  const void *kern = reinterpret_cast<const void *>(&decode_split_kernel<D, KB, VB, NB, NC>);
   const int resident = resident_workgroups(kern, dyn);
   if (resident < 0) return -1;
   const long long worst_tiles = static_cast<long long>(p.batch) * p.num_kv_heads * ((p.max_seq_len + kTile - 1) / kTile);
@@ -1379,16 +1405,16 @@ int split_grid(const DecodeParams &p) {
 }
 
 // launch = false: only the split grid, as waves (for sizing the partials).
-template <int D, int KB, int VB, int NB>
+template <int D, int KB, int VB, int NB, bool NC>
 long long launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s, bool launch) {
-  const int grid = split_grid<D, KB, VB, NB>(p);
+  const int grid = split_grid<D, KB, VB, NB, NC>(p);
   if (grid < 0) return -1;
   if (!launch) return static_cast<long long>(grid) * kWaves;
   if (p.batch == 0) return hipSuccess;
   const int qd = static_cast<int>(q_dtype);
   if (grid > 0) {
     const size_t dyn = static_cast<size_t>(p.batch + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, NB>), dim3(grid), dim3(64 * kWaves), dyn, s, p, qd);
+    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, NB, NC>), dim3(grid), dim3(64 * kWaves), dyn, s, p, qd);
     const int err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -1402,26 +1428,33 @@ long long launch_decode_t(tq_dtype q_dtype, const DecodeParams &p, hipStream_t s
   return hipGetLastError();
 }
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, bool NC>
 long long dispatch_decode_group(tq_dtype qd, const DecodeParams &p, hipStream_t s, bool launch) {
   const int G = p.num_q_heads / p.num_kv_heads;
-  if (G <= 4) return launch_decode_t<D, KB, VB, 4>(qd, p, s, launch);
-  if (G <= 8) return launch_decode_t<D, KB, VB, 2>(qd, p, s, launch);
-  return launch_decode_t<D, KB, VB, 1>(qd, p, s, launch);
+  if (G <= 4) return launch_decode_t<D, KB, VB, 4, NC>(qd, p, s, launch);
+  if (G <= 8) return launch_decode_t<D, KB, VB, 2, NC>(qd, p, s, launch);
+  return launch_decode_t<D, KB, VB, 1, NC>(qd, p, s, launch);
+}
+
+// norm correction applies to MSE keys only
+template <int D, int KB, int VB>
+long long dispatch_decode_nc(tq_dtype qd, const DecodeParams &p, hipStream_t s, bool launch) {
+  if (KB != 8 && p.norm_correction) return dispatch_decode_group<D, KB, VB, KB != 8>(qd, p, s, launch);
+  return dispatch_decode_group<D, KB, VB, false>(qd, p, s, launch);
 }
 
 template <int D>
 long long dispatch_decode_bits(const tq_config &c, tq_dtype qd, const DecodeParams &p, hipStream_t s, bool launch) {
   const int kb = c.key_quant_bits, vb = c.value_quant_bits;
-  if (kb == 3 && vb == 2) return dispatch_decode_group<D, 3, 2>(qd, p, s, launch);
-  if (kb == 4 && vb == 2) return dispatch_decode_group<D, 4, 2>(qd, p, s, launch);
-  if (kb == 8 && vb == 2) return dispatch_decode_group<D, 8, 2>(qd, p, s, launch);
-  if (kb == 3 && vb == 3) return dispatch_decode_group<D, 3, 3>(qd, p, s, launch);
-  if (kb == 3 && vb == 4) return dispatch_decode_group<D, 3, 4>(qd, p, s, launch);
-  if (kb == 4 && vb == 3) return dispatch_decode_group<D, 4, 3>(qd, p, s, launch);
-  if (kb == 4 && vb == 4) return dispatch_decode_group<D, 4, 4>(qd, p, s, launch);
-  if (kb == 8 && vb == 3) return dispatch_decode_group<D, 8, 3>(qd, p, s, launch);
-  if (kb == 8 && vb == 4) return dispatch_decode_group<D, 8, 4>(qd, p, s, launch);
+  if (kb == 3 && vb == 2) return dispatch_decode_nc<D, 3, 2>(qd, p, s, launch);
+  if (kb == 4 && vb == 2) return dispatch_decode_nc<D, 4, 2>(qd, p, s, launch);
+  if (kb == 8 && vb == 2) return dispatch_decode_nc<D, 8, 2>(qd, p, s, launch);
+  if (kb == 3 && vb == 3) return dispatch_decode_nc<D, 3, 3>(qd, p, s, launch);
+  if (kb == 3 && vb == 4) return dispatch_decode_nc<D, 3, 4>(qd, p, s, launch);
+  if (kb == 4 && vb == 3) return dispatch_decode_nc<D, 4, 3>(qd, p, s, launch);
+  if (kb == 4 && vb == 4) return dispatch_decode_nc<D, 4, 4>(qd, p, s, launch);
+  if (kb == 8 && vb == 3) return dispatch_decode_nc<D, 8, 3>(qd, p, s, launch);
+  if (kb == 8 && vb == 4) return dispatch_decode_nc<D, 8, 4>(qd, p, s, launch);
   return launch ? hipErrorInvalidValue : -1;
 }
 
