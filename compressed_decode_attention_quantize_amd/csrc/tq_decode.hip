@@ -35,6 +35,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <type_traits>
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -115,7 +116,7 @@ __device__ __forceinline__ void load_lds_16s(const void *sbase, uint32_t voff, u
       "s_mov_b32 m0, %0\n\t"
       "global_load_lds_dwordx4 %1, %2"
       :
-      : "s"(lds_base), "v"(voff), "s"(sbase)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(sbase)
       : "memory", "m0");
 }
 
@@ -368,22 +369,15 @@ __device__ __forceinline__ void key_operand(const uint32_t *words, uint32_t off,
   }
 }
 
-// Lane l takes a if bit l of the lane mask m is set, else b: one
-// v_cndmask_b32, kept from the compiler, which otherwise may turn a
-// lane-dependent select whose arms differ in cost into a divergent branch.
+// Lane l takes a if bit l of the lane mask m is set, else b (one
+// v_cndmask_b32 with the mask bit as the lane's condition; the arms are
+// values already in registers, so the compiler has no reason to branch).
 // Masks of loop-invariant conditions are computed once, outside the loops.
-// Never pass an MFMA result straight in: the compiler inserts no MFMA
-// hazard wait states before inline asm.
-__device__ __forceinline__ float mask_select(uint64_t m, float a, float b) {
-  float r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
-  return r;
+__device__ __forceinline__ bool mask_bit(uint64_t m) {
+  return (m >> __lane_id()) & 1ull;
 }
-__device__ __forceinline__ uint32_t mask_select(uint64_t m, uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
-  return r;
-}
+__device__ __forceinline__ float mask_select(uint64_t m, float a, float b) { return mask_bit(m) ? a : b; }
+__device__ __forceinline__ uint32_t mask_select(uint64_t m, uint32_t a, uint32_t b) { return mask_bit(m) ? a : b; }
 __device__ __forceinline__ uint64_t lane_mask(bool c) { return __builtin_amdgcn_ballot_w64(c); }
 // Lanes whose column (lane % 16) is below n, for 0 <= n <= 16.
 __device__ __forceinline__ uint64_t column_mask(int n) {
@@ -704,17 +698,23 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   // this wave's staging area in LDS (wave-uniform)
   const uint32_t stage_base = lds_offset(stage[0]) + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) *
                                                          (GE::stage_bytes(kBufs) / 4 * 4);
-  auto issue = [&](int bsel) {
-    const int rel = nx_blk - blk_base;
-    int phys;
-    if (rel >= 64) {
-      // refill the window; the wait for this load stays on this branch
+  // refill the window of block ids so that it covers the next `ahead`
+  // logical blocks from nx_blk
+  auto cover = [&](int ahead) __attribute__((always_inline)) {
+    if (nx_blk - blk_base + ahead > 64) {
       blk_base = nx_blk;
       blk_lane = blk_base + lane < p.max_blocks_per_seq ? bt_row[blk_base + lane] : 0;
-      phys = __builtin_amdgcn_readlane(blk_lane, 0);
-    } else {
-      phys = __builtin_amdgcn_readlane(blk_lane, rel);
+      // the wait for this load stays on this (rare) path: after the branch
+      // the compiler would otherwise wait for every load in flight
+      wait_vmcnt<0>();
     }
+  };
+  // kCovered: the window is known to hold the block (full macro tiles check
+  // once for all their tiles)
+  auto issue = [&](int bsel, auto covered) __attribute__((always_inline)) {
+    constexpr bool kCovered = decltype(covered)::value;
+    if constexpr (!kCovered) cover(1);
+    const int phys = __builtin_amdgcn_readlane(blk_lane, nx_blk - blk_base);
     ok_next = static_cast<uint32_t>(phys) < nblk;
     // an invalid block reads the pool's first block instead (its tokens are masked)
     const uint8_t *src = head_base + static_cast<uint64_t>(ok_next ? static_cast<uint32_t>(phys) : 0u) * blk_stride +
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       if (c < GE::kTileChunks) load_lds_16s(src, static_cast<uint32_t>(16 * c), dst + 1024 * k);
     }
   };
-  issue(0);  // waits for the query plane reads before overwriting it
+  issue(0, std::false_type{});  // waits for the query plane reads before overwriting it
 
   const float c0 = static_cast<float>(VX::kC0);
   const float inv_sigma = 1.0f / p.centroid_scale;
@@ -741,7 +741,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   // LDS byte offset of element group col's value codes in token 4kq's slot
   const uint32_t val_off = static_cast<uint32_t>(4 * kq * S + GE::kKeyBytes + VB * col);
   const uint32_t val_off_rd = static_cast<uint32_t>(4 * kq * S + GE::kKeyBytes + VB * min(col, GE::kGroups - 1));
-  for (int mt0 = begin; mt0 < end; mt0 += NT * kTile) {
+  // One macro tile. kFull: all NT tiles are inside the range and a tile
+  // follows them, so no tile needs a bounds check and every tile issues the
+  // next load; one branch-free basic block the compiler can schedule as a
+  // whole. The range's last macro tile takes the checked form.
+  auto macro_tile = [&](const int mt0, auto full) __attribute__((always_inline)) {
+    constexpr bool kFull = decltype(full)::value;
+    if constexpr (kFull) cover(NT);
     uint32_t vraw[kValLds ? 1 : NT][4];
     int tbuf[NT];  // buffer of tile i (wave-uniform)
     float4_t sraw[TL];
@@ -752,12 +758,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int tile0 = mt0 + i * kTile;
-      if (tile0 < end) {
-        const int ntok = min(kTile, end - tile0);
+      if (kFull || tile0 < end) {
+        const int ntok = kFull ? kTile : min(kTile, end - tile0);
         const bool tile_ok = ok_next;
         const int nsel = bsel + 1 == kBufs ? 0 : bsel + 1;
-        if (tile0 + kTile < end) {
-          issue(nsel);
+        if (kFull || tile0 + kTile < end) {
+          issue(nsel, std::integral_constant<bool, kFull>{});
           wait_vmcnt<kLoads>();  // this tile's loads are done, the next tile's may run
         } else {
           wait_vmcnt<0>();
@@ -850,6 +856,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         // workgroup left there (packed slot bytes can read as Inf or NaN)
         tokf[wave][kq][i][col] = kq == 0 ? -1.0f : (kq == 3 ? 1.0f : 0.0f);
         tbuf[i] = 0;
+        if constexpr (!kValLds) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vraw[i][r] = 0u;
+        }
       }
     }
 
@@ -956,8 +966,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     }
 #pragma unroll
     for (int i = 0; i < NT; i += 2) {
-      if (mt0 + i * kTile < end) {
-        const bool has1 = mt0 + (i + 1) * kTile < end;
+      if (kFull || mt0 + i * kTile < end) {
         if constexpr (kFold) {
           // K rows of tile t: hi weights in group t, lo weights in group
           // (t + NB/2) mod NB, zero elsewhere
@@ -970,10 +979,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
           bw[2] = pick(i + 1, 0);
           bw[3] = pick(i + 1, 1);
           const half8_t pv = __builtin_bit_cast(half8_t, bw);
+          // both tiles' fields in flight together; past the end of the range
+          // the second tile's weights are zero (masked tokens) and its buffer
+          // holds finite codes of some tile
           typename VX::Prep p0, p1;
           prep_tile(i, p0);
-          if (has1) prep_tile(i + 1, p1);
-          else p1 = p0;
+          prep_tile(i + 1, p1);
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             const half8_t av = __builtin_shufflevector(VX::get(p0, c), VX::get(p1, c), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -1007,9 +1018,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         typename VX::Prep p0, p1;
         prep_tile(i, p0);
         // past the end of the range the second half's weights are zero
-        // (masked tokens), so any finite codes do: reuse the first tile's
-        if (has1) prep_tile(i + 1, p1);
-        else p1 = p0;
+        // (masked tokens) and its buffer holds finite codes of some tile
+        prep_tile(i + 1, p1);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const half8_t av = __builtin_shufflevector(VX::get(p0, c), VX::get(p1, c), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -1019,7 +1029,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       }
     }
     __builtin_amdgcn_s_setprio(0);
-  }
+  };
+  int mt0 = begin;
+  for (; mt0 + NT * kTile < end; mt0 += NT * kTile) macro_tile(mt0, std::true_type{});
+  if (mt0 < end) macro_tile(mt0, std::false_type{});
 
   // ---- partial (m, l, acc + zero terms) of query head col
   l_lane = column_sum(l_lane);
