@@ -126,51 +126,45 @@ TQ_EXPORT tq_status tq_ring_append(const tq_config *cfg, const uint16_t *k_new, 
 
 namespace {
 
-// Workspace layout of a continuation prefill (offsets aligned to 256 bytes).
+// Work division and workspace of a continuation prefill. Row blocks of
+// kPrefillRows query rows per (sequence, KV head); the history is cut into
+// `splits` ranges of split_tokens tokens so that about kPrefillTargetWaves
+// waves run (no range shorter than kPrefillMinSplitTokens). The workspace
+// holds one partial per (row, split).
+constexpr int64_t kPrefillTargetWaves = 2048;
+constexpr int64_t kPrefillMinSplitTokens = 1024;
+
 struct PrefillLayout {
-  int row_groups = 0, vbatch = 0, split_tokens = 0;
-  size_t vq = 0, vtables = 0, vseq = 0, vring = 0, rows = 0, ring_k = 0, ring_v = 0, vout = 0, dec = 0, total = 0;
-  SplitPlan plan;
+  int row_blocks = 0, rows_pad = 0, splits = 1, split_tokens = 32, waves = 0;
+  size_t total = 0;
 };
 
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
 tq_status prefill_layout(const tq_config &cfg, int batch, int num_q_heads, int num_kv_heads, int max_chunk,
-                         int max_hist, int max_blocks, int q_elem_bytes, PrefillLayout *L) {
-  const int group = num_q_heads / num_kv_heads;
-  const int64_t rg = (static_cast<int64_t>(max_chunk) * group + 15) / 16;
-  const int64_t vb = static_cast<int64_t>(batch) * rg;
-  if (vb > 8192)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_prefill: batch * ceil(max_chunk * group / 16) must be at most 8192 "
-                                    "(split the chunk)");
-  L->row_groups = static_cast<int>(rg);
-  L->vbatch = static_cast<int>(vb);
-  // a wave covers at least a quarter of the longest history: few partial slots
-  L->split_tokens = std::max(256, (max_hist / 4 + 15) / 16 * 16);
-  const int hq = num_kv_heads * 16;
-  const int d = cfg.head_dim;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off = align256(off + bytes);
-    return at;
-  };
-  L->vq = take(static_cast<size_t>(vb) * hq * d * q_elem_bytes);
-  L->vtables = take(static_cast<size_t>(vb) * std::max(max_blocks, 1) * 4);
-  L->vseq = take(static_cast<size_t>(vb) * 4);
-  L->vring = take(static_cast<size_t>(vb) * 4);
-  L->rows = take(static_cast<size_t>(vb) * hq * 4);
-  L->ring_k = take(static_cast<size_t>(batch) * num_kv_heads * max_chunk * d * 2);
-  L->ring_v = take(static_cast<size_t>(batch) * num_kv_heads * max_chunk * d * 2);
-  L->vout = take(static_cast<size_t>(vb) * hq * d * 4);
-  const tq_status st = plan_decode(cfg, L->vbatch, hq, max_hist, max_chunk, L->split_tokens, &L->plan);
-  if (st != TQ_OK) return st;
-  L->dec = take(L->plan.workspace_bytes);
-  L->total = off;
+                         int max_hist, PrefillLayout *L) {
+  const int64_t group = num_q_heads / num_kv_heads;
+  const int64_t rows = static_cast<int64_t>(max_chunk) * group;
+  if (rows > INT32_MAX - kPrefillRows)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_prefill: max_chunk * (num_q_heads / num_kv_heads) must fit in 31 bits");
+  const int64_t rb = (rows + kPrefillRows - 1) / kPrefillRows;
+  const int64_t base = static_cast<int64_t>(batch) * num_kv_heads * rb;
+  int64_t splits = 1, split_tokens = 32;
+  if (max_hist > 0 && base > 0) {
+    splits = std::max<int64_t>(1, std::min<int64_t>((kPrefillTargetWaves + base - 1) / base,
+                                                    max_hist / kPrefillMinSplitTokens));
+    split_tokens = ((max_hist + splits - 1) / splits + 31) / 32 * 32;
+    splits = (max_hist + split_tokens - 1) / split_tokens;
+  }
+  const int64_t waves = base * splits;
+  if (waves > INT32_MAX - 64)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_prefill: too many (sequence, KV head, row block) work items; split the batch");
+  L->row_blocks = static_cast<int>(rb);
+  L->rows_pad = static_cast<int>(rb * kPrefillRows);
+  L->splits = static_cast<int>(splits);
+  L->split_tokens = static_cast<int>(split_tokens);
+  L->waves = static_cast<int>(waves);
+  L->total = static_cast<size_t>(batch) * num_kv_heads * L->rows_pad * L->splits * (cfg.head_dim + 4) * sizeof(float);
   return TQ_OK;
 }
-
-int dtype_bytes(tq_dtype d) { return d == TQ_F32 ? 4 : 2; }
 
 }  // namespace
 
@@ -184,8 +178,7 @@ TQ_EXPORT tq_status tq_prefill_workspace_size(const tq_config *cfg, int batch, i
       max_hist < 0 || max_blocks_per_seq < 0 || !valid_dtype(q_dtype))
     return fail(TQ_ERR_INVALID_ARG, "tq_prefill_workspace_size: invalid sizes or dtype");
   PrefillLayout L;
-  st = prefill_layout(*cfg, batch, num_q_heads, num_kv_heads, max_chunk, max_hist, max_blocks_per_seq,
-                      dtype_bytes(q_dtype), &L);
+  st = prefill_layout(*cfg, batch, num_q_heads, num_kv_heads, max_chunk, max_hist, &L);
   if (st != TQ_OK) return st;
   *bytes_out = L.total;
   return TQ_OK;
@@ -213,82 +206,47 @@ TQ_EXPORT tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx, co
     return fail(TQ_ERR_INVALID_ARG, "tq_prefill_attention: NULL pointer");
   if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(kv_pool) || !aligned16(out))
     return fail(TQ_ERR_INVALID_ARG, "tq_prefill_attention: q, k_chunk, v_chunk, kv_pool and out must be 16-byte aligned");
+  if (max_hist > 0 && num_blocks < 1)
+    return fail(TQ_ERR_INVALID_ARG, "tq_prefill_attention: a history (max_hist > 0) needs a pool of at least one block");
   PrefillLayout L;
-  st = prefill_layout(*cfg, batch, num_q_heads, num_kv_heads, max_chunk, max_hist, max_blocks_per_seq,
-                      dtype_bytes(q_dtype), &L);
+  st = prefill_layout(*cfg, batch, num_q_heads, num_kv_heads, max_chunk, max_hist, &L);
   if (st != TQ_OK) return st;
   if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(TQ_ERR_WORKSPACE, "tq_prefill_attention: workspace must be 256-byte aligned and hold " +
                                       std::to_string(L.total) + " bytes");
-  char *ws = static_cast<char *>(workspace);
-  PrefillParams pp;
-  std::memset(&pp, 0, sizeof(pp));
-  pp.q = q;
-  pp.k_chunk = k_chunk;
-  pp.v_chunk = v_chunk;
-  pp.cu_chunk = cu_chunk;
-  pp.hist_lens = hist_lens;
-  pp.block_tables = block_tables;
-  pp.out = out;
-  pp.vq = ws + L.vq;
-  pp.vtables = reinterpret_cast<int32_t *>(ws + L.vtables);
-  pp.vseq_lens = reinterpret_cast<int32_t *>(ws + L.vseq);
-  pp.vring_lens = reinterpret_cast<int32_t *>(ws + L.vring);
-  pp.row_lens = reinterpret_cast<int32_t *>(ws + L.rows);
-  pp.ring_k = reinterpret_cast<uint16_t *>(ws + L.ring_k);
-  pp.ring_v = reinterpret_cast<uint16_t *>(ws + L.ring_v);
-  pp.vout = reinterpret_cast<float *>(ws + L.vout);
-  pp.q_elem_bytes = dtype_bytes(q_dtype);
-  pp.batch = batch;
-  pp.vbatch = L.vbatch;
-  pp.row_groups = L.row_groups;
-  pp.group = num_q_heads / num_kv_heads;
-  pp.num_q_heads = num_q_heads;
-  pp.num_kv_heads = num_kv_heads;
-  pp.head_dim = cfg->head_dim;
-  pp.max_chunk = max_chunk;
-  pp.max_blocks_per_seq = max_blocks_per_seq;
-  int err = launch_prefill_prep(pp, stream);
-  if (err != hipSuccess) return hip_fail("tq_prefill_attention layout launch", err);
-
-  DecodeParams p;
+  PrefillParams p;
   std::memset(&p, 0, sizeof(p));
-  p.q = pp.vq;
+  p.q = q;
+  p.k_chunk = k_chunk;
+  p.v_chunk = v_chunk;
+  p.cu_chunk = cu_chunk;
+  p.hist_lens = hist_lens;
+  p.block_tables = block_tables;
   p.pool = kv_pool;
-  p.block_tables = pp.vtables;
-  p.seq_lens = pp.vseq_lens;
-  p.ring_k = pp.ring_k;
-  p.ring_v = pp.ring_v;
-  p.ring_lens = pp.vring_lens;
-  p.out = pp.vout;
+  p.partials = static_cast<float *>(workspace);
+  p.out = out;
   p.num_blocks = num_blocks;
-  p.batch = L.vbatch;
-  p.num_q_heads = num_kv_heads * 16;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.max_chunk = max_chunk;
+  p.max_hist = max_hist;
   p.block_size = block_size;
   p.max_blocks_per_seq = max_blocks_per_seq;
-  p.max_seq_len = max_hist;
-  p.ring_cap = max_chunk;
-  p.split_tokens = L.plan.split_tokens;
-  p.ring_chunks = L.plan.ring_chunks;
-  p.plan = reinterpret_cast<int32_t *>(ws + L.dec);
-  p.partials = reinterpret_cast<float *>(ws + L.dec + L.plan.header_bytes);
-  p.ring_partials = reinterpret_cast<float *>(ws + L.dec + L.plan.ring_offset);
-  p.slot_bytes = cfg->slot_size_aligned;
-  p.key_bytes = cfg->key_packed_size;
-  p.norm_correction = cfg->norm_correction;
+  p.row_blocks = L.row_blocks;
+  p.rows_pad = L.rows_pad;
+  p.splits = L.splits;
+  p.split_tokens = L.split_tokens;
+  p.waves = L.waves;
   const float scale = softmax_scale > 0.0f ? softmax_scale
                                            : static_cast<float>(1.0 / std::sqrt(static_cast<double>(cfg->head_dim)));
   p.scale_log2 = scale * 1.4426950408889634f;
   p.centroid_scale = cfg->centroid_scale;
   layer_sign_mask(*cfg, layer_idx, p.sign_words);
   for (int i = 0; i < 16; ++i) p.centroids[i] = cfg->centroids[i];
-  p.ring_group = L.row_groups;
-  p.ring_row_lens = pp.row_lens;
-  err = launch_decode(*cfg, q_dtype, p, stream);
-  if (err != hipSuccess) return hip_fail("tq_prefill_attention attention launch", err);
-  err = launch_prefill_scatter(pp, stream);
-  if (err != hipSuccess) return hip_fail("tq_prefill_attention scatter launch", err);
+  const int err = launch_prefill(*cfg, q_dtype, p, stream);
+  if (err != hipSuccess) return hip_fail("tq_prefill_attention launch", err);
   return TQ_OK;
 }
 

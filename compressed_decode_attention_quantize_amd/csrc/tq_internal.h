@@ -112,38 +112,43 @@ struct DecodeParams {
 
 // Launchers (defined in the kernel translation units). Return hipSuccess or a
 // HIP error code as int.
-// Continuation prefill: the chunk's query rows regrouped as virtual decode
-// sequences of 16 rows per KV head (workspace views in the lower half).
+// Continuation prefill: one wave per (sequence, KV head, history split, row
+// block of 16 * kPrefillRowGroups query rows); rows of a KV head are ordered
+// token-major (row r = t * group + g for query head h * group + g).
+constexpr int kPrefillRowGroups = 2;
+constexpr int kPrefillRows = 16 * kPrefillRowGroups;
 struct PrefillParams {
-  const void *q;
-  const uint16_t *k_chunk;
+  const void *q;             // [N][num_q_heads][D], q_dtype
+  const uint16_t *k_chunk;   // [N][num_kv_heads][D] bf16 bits
   const uint16_t *v_chunk;
-  const int32_t *cu_chunk;
-  const int32_t *hist_lens;
+  const int32_t *cu_chunk;   // [batch + 1]
+  const int32_t *hist_lens;  // [batch]
   const int32_t *block_tables;
-  float *out;
-  void *vq;             // [vbatch][Hkv * 16][D], q's dtype
-  int32_t *vtables;     // [vbatch][max_blocks_per_seq]
-  int32_t *vseq_lens;   // [vbatch]
-  int32_t *vring_lens;  // [vbatch]
-  int32_t *row_lens;    // [vbatch][Hkv * 16]
-  uint16_t *ring_k;     // [batch][Hkv][max_chunk][D]
-  uint16_t *ring_v;
-  float *vout;          // [vbatch][Hkv * 16][D]
-  int32_t q_elem_bytes;
+  const uint8_t *pool;
+  // partials [batch][num_kv_heads][rows_pad][splits] x [m, l, -, -, acc[D]] fp32
+  float *partials;
+  float *out;                // [N][num_q_heads][D] fp32
+  int64_t num_blocks;
   int32_t batch;
-  int32_t vbatch;       // batch * row_groups
-  int32_t row_groups;   // ceil(max_chunk * group / 16)
-  int32_t group;        // query heads per KV head
   int32_t num_q_heads;
   int32_t num_kv_heads;
-  int32_t head_dim;
+  int32_t group;             // query heads per KV head
   int32_t max_chunk;
+  int32_t max_hist;
+  int32_t block_size;
   int32_t max_blocks_per_seq;
+  int32_t row_blocks;        // ceil(max_chunk * group / kPrefillRows)
+  int32_t rows_pad;          // row_blocks * kPrefillRows
+  int32_t splits;            // history ranges per row block
+  int32_t split_tokens;      // tokens per history range (multiple of 32)
+  int32_t waves;             // batch * num_kv_heads * splits * row_blocks
+  float scale_log2;          // softmax scale * log2(e)
+  float centroid_scale;      // sigma of the f16 centroid table
+  uint32_t sign_words[4];
+  float centroids[16];
 };
 
-int launch_prefill_prep(const PrefillParams &p, void *stream);
-int launch_prefill_scatter(const PrefillParams &p, void *stream);
+int launch_prefill(const tq_config &cfg, tq_dtype q_dtype, const PrefillParams &p, void *stream);
 int launch_quantize(const tq_config &cfg, tq_dtype dtype, const QuantParams &p, void *stream);
 int launch_dequant(const tq_config &cfg, const DequantParams &p, void *stream);
 int launch_ring_commit(int32_t *ring_lens, int32_t *seq_lens, int batch, int ring_cap, void *stream);

@@ -1,148 +1,725 @@
-// Continuation prefill over the compressed cache: layout kernels around the
-// decode kernels.
+// Continuation prefill over the compressed cache.
 //
 // Source: vLLM API page "vllm.model_executor.layers.quantization.turboquant",
 // TurboQuantConfig.mse_bits docstring (the centroid table is kept for
 // continuation-prefill dequant); attention of a chunk's tokens to the
 // history, as in direction 1 of the hnwysp.cn article on the stand-alone
-// turboquant project (query rotated forward, online softmax over blocks).
+// turboquant project (query rotated forward, online softmax over blocks,
+// no materialised FP16 KV); norm correction after the TurboQuantConfig
+// docstring.
 //
 // Token t of sequence b's chunk attends to the sequence's compressed history
-// and, causally, to the chunk's exact tokens 0..t. The query rows of one KV
-// head (chunk token x query head of that KV head, token-major) are cut into
-// groups of 16; each group is one "virtual sequence" of the decode kernels,
-// which fill all 16 MFMA columns with its rows:
-//   - the split kernel streams the history once per row group (its block
-//     table row and length are the sequence's),
-//   - the ring kernel attends to the chunk, stored once per sequence in the
-//     ring layout and shared by the sequence's row groups, each row cut at
-//     its own causal limit,
-//   - the reduce merges both into one fp32 row per virtual query head,
-// and a scatter puts the rows back in [token][head] order.
+// and, causally, to the chunk's exact bf16 tokens 0..t. The query rows of one
+// KV head are ordered token-major (row r = t * G + g for query head h G + g)
+// and cut into row blocks of R = 16 NG rows, one wave each: the wave decodes
+// every history tile once and multiplies it with its NG groups of 16 rows,
+// so a tile's key/value decode is shared by R rows instead of 16.
+//
+//  attention kernel (one wave per (sequence, KV head, history split, row block);
+//                four waves per workgroup sharing the code->f16 pair table)
+//     per 16-token history tile, staged HBM -> LDS one macro tile (two
+//     tiles) ahead:
+//       K~ = centroid values (MSE: pair table, FP8: hardware cvt), f16, once
+//       S^T[t][row] = K~ . (Pi q)^T        MFMA 16x16x32 f16 per row group,
+//                                          q as f16 hi + lo parts
+//       |c_t|^2 = diag(K~ K~^T)             (norm correction only), once
+//       online softmax in exp2 per row group
+//       Out^T[j][row] += (code_tj - c0)^T . (p_t s'_t)   MFMA 16x16x32 f16
+//                      over tile pairs, codes expanded once per tile pair,
+//                      weights as f16 hi + lo parts per row group
+//       zero terms += p_t (z'_t + c0 s'_t)
+//     the last history split of a row block then takes the chunk's exact
+//     tokens 0..t (bf16 MFMA 16x16x32, raw q and the weights as bf16 hi + lo
+//     parts, causal mask per row) into the same softmax state;
+//     writes an unnormalised partial (m, l, acc[D]) per (row, split).
+//  reduce kernel (log-sum-exp merge of a row's split partials, written to
+//                out[token][query head]).
 
 #include "tq_device.h"
 #include "tq_internal.h"
+#include "tq_mfma.h"
 
 namespace tq {
 namespace {
 
-constexpr int kThreads = 256;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-// q' [vb][h * 16 + c][D] <- q [cu[b] + t][h * G + g] with vb = b * rg + j,
-// row r = 16 j + c = t * G + g; rows past the chunk are zero. 16 bytes per
-// thread step (elem_bytes 2 or 4).
-__global__ __launch_bounds__(kThreads) void prefill_gather_q(PrefillParams p) {
-  const int64_t vec_per_row = static_cast<int64_t>(p.head_dim) * p.q_elem_bytes / 16;
-  const int64_t total = static_cast<int64_t>(p.vbatch) * p.num_kv_heads * 16 * vec_per_row;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t row = e / vec_per_row;  // vb * (Hkv * 16) + h * 16 + c
-    const int64_t x = e - row * vec_per_row;
-    const int vb = static_cast<int>(row / (p.num_kv_heads * 16));
-    const int hc = static_cast<int>(row - static_cast<int64_t>(vb) * p.num_kv_heads * 16);
-    const int h = hc / 16, c = hc % 16;
-    const int b = vb / p.row_groups;
-    const int r = (vb - b * p.row_groups) * 16 + c;
-    const int t = r / p.group, g = r % p.group;
-    const int c0 = p.cu_chunk[b], clen = p.cu_chunk[b + 1] - c0;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (t < clen) {
-      const int64_t src = (static_cast<int64_t>(c0 + t) * p.num_q_heads + h * p.group + g) * vec_per_row + x;
-      v = reinterpret_cast<const uint4 *>(p.q)[src];
+constexpr int kWaves = 4;       // waves per workgroup
+constexpr int kPad = 4;         // partial = [m, l, -, -, acc[D]]
+constexpr int kThreads = 256;   // reduce kernel
+constexpr float kLazy = 4.0f;   // reference-maximum slack of the online softmax (log2 units)
+
+__device__ __forceinline__ int pstride(int d) { return d + kPad; }
+
+// bf16 hi + lo parts of 8 floats (hi = RNE(x), lo = RNE(x - hi): 16
+// significant bits together).
+__device__ __forceinline__ void split_bf16(const float x[8], bf16x8_t &hi, bf16x8_t &lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = static_cast<__bf16>(x[e]);
+    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(hi[e]));
+  }
+}
+
+// 8 query elements (f32, bf16 or f16) as floats.
+__device__ __forceinline__ void load_q8(const void *q, int q_dtype, int64_t e0, bool live, float x[8]) {
+  if (q_dtype == TQ_F32) {
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const float *>(q) + e0);
+    const u32x4_t a = live ? src[0] : u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t b = live ? src[1] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = __uint_as_float(a[e]);
+      x[4 + e] = __uint_as_float(b[e]);
     }
-    reinterpret_cast<uint4 *>(p.vq)[e] = v;
-  }
-}
-
-// ring' [b][h][t][D] <- chunk [cu[b] + t][h][D] (bf16), zero past the chunk.
-__global__ __launch_bounds__(kThreads) void prefill_gather_chunk(PrefillParams p) {
-  const int64_t vec_per_row = p.head_dim / 8;
-  const int64_t total = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.max_chunk * vec_per_row;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t row = e / vec_per_row;  // (b * Hkv + h) * max_chunk + t
-    const int64_t x = e - row * vec_per_row;
-    const int t = static_cast<int>(row % p.max_chunk);
-    const int64_t bh = row / p.max_chunk;
-    const int h = static_cast<int>(bh % p.num_kv_heads);
-    const int b = static_cast<int>(bh / p.num_kv_heads);
-    const int c0 = p.cu_chunk[b], clen = p.cu_chunk[b + 1] - c0;
-    uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (t < clen) {
-      const int64_t src = (static_cast<int64_t>(c0 + t) * p.num_kv_heads + h) * vec_per_row + x;
-      kv = reinterpret_cast<const uint4 *>(p.k_chunk)[src];
-      vv = reinterpret_cast<const uint4 *>(p.v_chunk)[src];
-    }
-    reinterpret_cast<uint4 *>(p.ring_k)[e] = kv;
-    reinterpret_cast<uint4 *>(p.ring_v)[e] = vv;
-  }
-}
-
-// Per virtual sequence: its block-table row, history length and chunk length
-// (0 for a row group past the chunk), and each row's causal limit.
-__global__ __launch_bounds__(kThreads) void prefill_tables(PrefillParams p) {
-  const int vb = blockIdx.x;
-  const int b = vb / p.row_groups;
-  const int j = vb - b * p.row_groups;
-  const int c0 = p.cu_chunk[b], clen = p.cu_chunk[b + 1] - c0;
-  const bool live = 16 * j < clen * p.group;
-  for (int i = threadIdx.x; i < p.max_blocks_per_seq; i += blockDim.x)
-    p.vtables[static_cast<int64_t>(vb) * p.max_blocks_per_seq + i] =
-        p.block_tables[static_cast<int64_t>(b) * p.max_blocks_per_seq + i];
-  for (int hc = threadIdx.x; hc < p.num_kv_heads * 16; hc += blockDim.x) {
-    const int r = 16 * j + hc % 16;
-    const int t = r / p.group;
-    p.row_lens[static_cast<int64_t>(vb) * p.num_kv_heads * 16 + hc] = t < clen ? t + 1 : 0;
-  }
-  if (threadIdx.x == 0) {
-    p.vseq_lens[vb] = live ? max(p.hist_lens[b], 0) : 0;
-    p.vring_lens[vb] = live ? clen : 0;
-  }
-}
-
-// out [cu[b] + t][h * G + g][D] <- out' [vb][h * 16 + c][D].
-__global__ __launch_bounds__(kThreads) void prefill_scatter(PrefillParams p) {
-  const int64_t vec_per_row = p.head_dim / 4;
-  const int64_t total = static_cast<int64_t>(p.vbatch) * p.num_kv_heads * 16 * vec_per_row;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t row = e / vec_per_row;
-    const int64_t x = e - row * vec_per_row;
-    const int vb = static_cast<int>(row / (p.num_kv_heads * 16));
-    const int hc = static_cast<int>(row - static_cast<int64_t>(vb) * p.num_kv_heads * 16);
-    const int h = hc / 16, c = hc % 16;
-    const int b = vb / p.row_groups;
-    const int r = (vb - b * p.row_groups) * 16 + c;
-    const int t = r / p.group, g = r % p.group;
-    const int c0 = p.cu_chunk[b], clen = p.cu_chunk[b + 1] - c0;
-    if (t < clen) {
-      const int64_t dst = (static_cast<int64_t>(c0 + t) * p.num_q_heads + h * p.group + g) * vec_per_row + x;
-      reinterpret_cast<float4 *>(p.out)[dst] = reinterpret_cast<const float4 *>(p.vout)[e];
+  } else {
+    const u32x4_t a = live ? *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(q) + e0)
+                           : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (q_dtype == TQ_BF16) {
+        x[2 * e] = bf16_bits_to_float(a[e] & 0xffffu);
+        x[2 * e + 1] = bf16_bits_to_float(a[e] >> 16);
+      } else {
+        x[2 * e] = f16_bits_to_float(a[e] & 0xffffu);
+        x[2 * e + 1] = f16_bits_to_float(a[e] >> 16);
+      }
     }
   }
 }
 
-unsigned grid_for(int64_t items) {
-  const int64_t blocks = (items + kThreads - 1) / kThreads;
-  return static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks));
+// Plain v_max / v_min: the compiler puts a canonicalising max around
+// operands it cannot prove canonical (cross-lane moves, LDS reads); the
+// values here are finite or -inf. column_max_raw: maximum over the 4 lane
+// rows of an MFMA column (lanes c, c + 16, c + 32, c + 48) by the gfx950
+// row-swap permutes.
+__device__ __forceinline__ float fmax_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float fmin_raw(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float column_max_raw(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmax_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax_raw(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// f16 hi + lo parts of 4 weights (w0, w1 | w2, w3 packed pairs): hi rounded
+// toward zero, lo = w - hi rounded to f16 (|w - hi - lo| <= 2^-21 |w|). Each
+// residual is one mixed-precision multiply-add that reads its f16 half of hi
+// in place and writes its half of lo (v_fma_mixlo / v_fma_mixhi); the inputs
+// are ordinary VALU results.
+__device__ __forceinline__ void split_f16_pairs(const float w[4], uint32_t hw[2], uint32_t lw[2]) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    hw[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[2 * k], w[2 * k + 1]));
+    uint32_t lo;
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %3, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+        : "=&v"(lo)
+        : "v"(w[2 * k]), "v"(hw[k]), "v"(w[2 * k + 1]));
+    lw[k] = lo;
+  }
+}
+
+template <int D, int KB, int VB, int NG, bool NC>
+__global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams p, int q_dtype) {
+  using GE = Geo<D, KB, VB>;
+  using VX = ValueExpand<VB>;
+  constexpr int S = GE::kSlot;
+  constexpr int KM = GE::kKM;
+  constexpr int R = 16 * NG;        // query rows of a wave
+  constexpr int kBufs = 4;          // two pairs of tiles
+  constexpr int kLoads = GE::kChunksPerLane;
+  constexpr bool nc = GE::kMse && NC;
+
+  __shared__ uint32_t lut[GE::kLut];
+  __shared__ __align__(16) uint32_t stage[kWaves][GE::stage_bytes(kBufs) / 4];
+  // per-token scalars of the macro tile: norm * scale (< 0: masked), s', z' + c0 s', ||c||^2;
+  // plane 4 takes the writes of lanes that hold nothing for a plane
+  __shared__ __align__(16) float tokf[kWaves][5][2][16];
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int kq = lane >> 4;
+
+  if constexpr (GE::kMse) {
+    for (int e = threadIdx.x; e < GE::kLut; e += 64 * kWaves) {
+      const int lo = e & ((1 << KB) - 1), hi = e >> KB;
+      lut[e] = f16_pair_bits(p.centroids[lo] * p.centroid_scale, p.centroids[hi] * p.centroid_scale);
+    }
+  }
+  __syncthreads();  // the last workgroup barrier; waves are independent below
+
+  // ---- work item. Logical workgroups follow each other on one XCD (the
+  // hardware deals workgroups to the 8 XCDs in turn), so the row blocks that
+  // stream the same history share that XCD's L2.
+  int wg = blockIdx.x;
+  if ((gridDim.x & 7u) == 0) wg = (wg & 7) * static_cast<int>(gridDim.x >> 3) + (wg >> 3);
+  const int w = wg * kWaves + __builtin_amdgcn_readfirstlane(wave);
+  if (w >= p.waves) return;
+  const int rb = w % p.row_blocks;
+  int rest = w / p.row_blocks;
+  const int s = rest % p.splits;
+  rest /= p.splits;
+  const int h = rest % p.num_kv_heads;
+  const int b = rest / p.num_kv_heads;
+  const int G = p.group;
+  const int Hq = p.num_q_heads;
+  const int c0 = p.cu_chunk[b];
+  const int clen = min(max(p.cu_chunk[b + 1] - c0, 0), p.max_chunk);
+  const int row0 = rb * R;
+  const int nrows = clen * G;
+  if (row0 >= nrows) return;  // no live row: the reduce reads nothing of this block
+  const int seq_cap = min(p.max_hist, p.max_blocks_per_seq * p.block_size);
+  const int hist = min(max(p.hist_lens[b], 0), seq_cap);
+  const int t_begin = min(hist, s * p.split_tokens);
+  const int t_end = s == p.splits - 1 ? hist : min(hist, t_begin + p.split_tokens);
+
+  uint32_t *scr = stage[wave];  // this wave's LDS: queries, then the staged tiles
+
+  // ---- rotated query rows as f16 hi + lo parts in the MFMA B-operand
+  // layout, one plane pass per row group: column n of group i is row
+  // row0 + 16 i + n (zero past the chunk).
+  half8_t qf[NG][KM], ql[NG][KM];
+  {
+    using T = Team<D>;
+    const int team = lane / T::kLanes;
+    const int r = lane - team * T::kLanes;
+    constexpr int rows_per_pass = T::kPerWave;
+    constexpr int kPasses = (16 + rows_per_pass - 1) / rows_per_pass;
+    _Float16 *qs = reinterpret_cast<_Float16 *>(scr);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      u32x4_t qhi[kPasses], qlo[kPasses];
+      float xs[kPasses][8];
+#pragma unroll
+      for (int k = 0; k < kPasses; ++k) {
+        const int g = k * rows_per_pass + team;
+        const int row = row0 + 16 * gi + g;
+        const bool live = team < rows_per_pass && g < 16 && row < nrows;
+        const int t = row / G;
+        const int64_t e0 = (static_cast<int64_t>(c0 + (live ? t : 0)) * Hq + h * G + (live ? row - t * G : 0)) * D + 8 * r;
+        load_q8(p.q, q_dtype, e0, live, xs[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < kPasses; ++k) {
+        float *x = xs[k];
+        if constexpr (GE::kMse) {
+          const uint32_t sb = lane_sign_bits(p.sign_words, r);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = flip_sign(x[e], (sb >> e) & 1u);
+          team_wht<D>(x, r % T::kBlockLanes);
+          const float rb_scale = rsqrtf(static_cast<float>(T::kBlock));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] *= rb_scale;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qhi[k][e] = f16_pair_bits(x[2 * e], x[2 * e + 1]);
+          qlo[k][e] = f16_pair_bits(x[2 * e] - f16_bits_to_float(qhi[k][e] & 0xffffu),
+                                    x[2 * e + 1] - f16_bits_to_float(qhi[k][e] >> 16));
+        }
+      }
+#pragma unroll
+      for (int phase = 0; phase < 2; ++phase) {
+        wave_lds_sync();  // earlier reads of the plane (other lanes) are done
+#pragma unroll
+        for (int k = 0; k < kPasses; ++k) {
+          const int g = k * rows_per_pass + team;
+          if (team < rows_per_pass && g < 16)
+            *reinterpret_cast<u32x4_t *>(qs + g * D + 8 * r) = phase == 0 ? qhi[k] : qlo[k];
+        }
+        wave_lds_sync();  // the rows other lanes wrote are visible
+#pragma unroll
+        for (int m = 0; m < KM; ++m) {
+          const half8_t v = *reinterpret_cast<const half8_t *>(qs + col * D + kq * (D / 4) + 8 * m);
+          if (phase == 0) qf[gi][m] = v;
+          else ql[gi][m] = v;
+        }
+      }
+    }
+  }
+
+  float4_t acc[NG][8];
+  float m_run[NG], l_lane[NG], z_lane[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[gi][c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run[gi] = -INFINITY;
+    l_lane[gi] = 0.0f;
+    z_lane[gi] = 0.0f;
+  }
+  // Online softmax with a lazy reference maximum: weights are exp2(s - m_run)
+  // with m_run moved only when a column's maximum exceeds it by more than
+  // kLazy (weights up to 2^kLazy; the normalisation by l cancels the
+  // reference), so the rescale of the accumulators is a rare branch.
+  auto rescale = [&](int gi, float mt) __attribute__((always_inline)) {
+    const float mn = fmaxf(m_run[gi], mt);
+    const float alpha = mn == -INFINITY ? 1.0f : exp2f(m_run[gi] - mn);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[gi][c] *= alpha;
+    l_lane[gi] *= alpha;
+    z_lane[gi] *= alpha;
+    m_run[gi] = mn;
+  };
+
+  // ---- history: tiles HBM -> LDS by direct loads (lane l of a load
+  // instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS window), in
+  // pairs of tiles, two pair buffers per wave: the next pair is in flight
+  // while this one is used.
+  if (t_begin < t_end) {
+    const int32_t *bt_row = p.block_tables + static_cast<int64_t>(b) * p.max_blocks_per_seq;
+    int nx_blk = t_begin / p.block_size;
+    int nx_off = t_begin - nx_blk * p.block_size;
+    int nx_tok = t_begin;  // first token of the next tile to load
+    // block ids of the range, 64 at a time (lane i: logical block blk_base + i)
+    int blk_base = nx_blk;
+    int blk_lane = blk_base + lane < p.max_blocks_per_seq ? bt_row[blk_base + lane] : 0;
+    const uint32_t blk_stride = static_cast<uint32_t>(p.num_kv_heads * p.block_size * S);
+    const uint8_t *head_base = p.pool + static_cast<int64_t>(h) * p.block_size * S;
+    const uint32_t nblk = static_cast<uint32_t>(p.num_blocks < 0x7fffffff ? p.num_blocks : 0x7fffffff);
+    const uint32_t stage_base = lds_offset(stage[0]) + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) *
+                                                           (GE::stage_bytes(kBufs) / 4 * 4);
+    const uint8_t *src = head_base;  // the last tile's source
+    uint32_t tile_ok = 0;            // bit k: buffer k holds a tile of a valid block
+    // the block-id window covers the blocks of the next two tiles
+    auto cover = [&]() __attribute__((always_inline)) {
+      if (nx_blk - blk_base + 2 > 64) {
+        blk_base = nx_blk;
+        blk_lane = blk_base + lane < p.max_blocks_per_seq ? bt_row[blk_base + lane] : 0;
+        wait_vmcnt<0>();
+      }
+    };
+    // Loads the next tile into buffer bsel. A tile past the range reloads the
+    // last source, so every pair issues the same number of loads, and is
+    // masked.
+    auto issue = [&](int bsel) __attribute__((always_inline)) {
+      const bool live = nx_tok < t_end;
+      const int phys = __builtin_amdgcn_readlane(blk_lane, min(nx_blk - blk_base, 63));
+      const bool ok = live && static_cast<uint32_t>(phys) < nblk;
+      // an invalid block reads the pool's first block instead (its tokens are masked)
+      const uint8_t *fresh = head_base + static_cast<uint64_t>(ok ? static_cast<uint32_t>(phys) : 0u) * blk_stride +
+                             static_cast<uint32_t>(nx_off * S);
+      src = live ? fresh : src;
+      tile_ok = (tile_ok & ~(1u << bsel)) | ((ok ? 1u : 0u) << bsel);
+      const int adv = live ? kTile : 0;
+      nx_tok += adv;
+      nx_off += adv;
+      const bool wrap = nx_off == p.block_size;
+      nx_blk += wrap ? 1 : 0;
+      nx_off = wrap ? 0 : nx_off;
+      const uint32_t dst = stage_base + bsel * GE::kTileBuf;
+      wait_lds_reads();  // earlier reads of this buffer (or the query plane) have executed
+#pragma unroll
+      for (int k = 0; k < kLoads; ++k) {
+        const int c = lane + 64 * k;
+        if (c < GE::kTileChunks) load_lds_16s(src, static_cast<uint32_t>(16 * c), dst + 1024 * k);
+      }
+    };
+
+    const float c0f = static_cast<float>(VX::kC0);
+    const float inv_sigma = 1.0f / p.centroid_scale;
+    const uint64_t m_kq0 = lane_mask(kq == 0), m_kq1 = lane_mask(kq == 1), m_kq3 = lane_mask(kq == 3);
+    const int diag_r = col - 4 * kq;
+    const float dsel0 = diag_r == 0 ? 1.0f : 0.0f, dsel1 = diag_r == 1 ? 1.0f : 0.0f;
+    const float dsel2 = diag_r == 2 ? 1.0f : 0.0f, dsel3 = diag_r == 3 ? 1.0f : 0.0f;
+    const uint32_t val_off_rd = static_cast<uint32_t>(4 * kq * S + GE::kKeyBytes + VB * min(col, GE::kGroups - 1));
+
+    cover();
+    issue(0);
+    issue(1);
+    int cur = 0;
+    for (int pt = t_begin; pt < t_end; pt += 2 * kTile) {
+      float sv[NG][2][4], mt[NG];
+      float4_t s1v[2], zcv[2];
+      {
+        {
+          const int nxt = cur ^ 2;
+          cover();
+          issue(nxt);
+          issue(nxt + 1);
+          wait_vmcnt<2 * kLoads>();  // this pair's loads are done, the next pair's may run
+
+          // ---- phase A, per tile: the key operand once, the scores of
+          // every row group, per-token scalars to LDS
+          float4_t sraw[NG][2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int bsel = cur + u;
+            const uint32_t *tw = scr + bsel * (GE::kTileBuf / 4);
+            const int ntok = min(max(t_end - (pt + u * kTile), 0), kTile);
+            const bool tile_valid = (tile_ok >> bsel) & 1u;
+            constexpr uint32_t kScaleOff = GE::kKeyBytes + GE::kValCodeBytes;
+            uint32_t x;
+            {
+              const uint16_t *hh = reinterpret_cast<const uint16_t *>(tw);
+              const uint32_t off = static_cast<uint32_t>(col * S) + (kq == 0 ? GE::kKeyCodeBytes : kScaleOff);
+              x = static_cast<uint32_t>(hh[off >> 1]) | (static_cast<uint32_t>(hh[(off >> 1) + 1]) << 16);
+            }
+            half8_t kf[KM];
+            key_operand<D, KB, VB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
+            {
+              // plane kq of token col: norm * scale (-inf: masked), s', z' + c0 s', 1
+              const float a = f16_bits_to_float(x & 0xffffu);
+              const float z1 = f16_bits_to_float(x >> 16);
+              const uint64_t ok = tile_valid ? column_mask(ntok) : 0ull;
+              const float fb = GE::kMse ? p.scale_log2 * a : p.scale_log2;
+              const float val_k = mask_select(ok, fb, -INFINITY);
+              const float val_v = mask_select(ok, mask_select(m_kq1, a, fmaf(c0f, a, z1)), 0.0f);
+              float val = mask_select(m_kq0, val_k, val_v);
+              val = mask_select(m_kq3, 1.0f, val);
+              tokf[wave][kq][u][col] = val;
+            }
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+              float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int m = 0; m < KM; ++m) {
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[gi][m], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], ql[gi][m], sc, 0, 0, 0);
+              }
+              sraw[gi][u] = sc;
+            }
+            if constexpr (nc) {
+              // ||c_t||^2 of token t = 4kq + r on the Gram diagonal: lane (kq,
+              // col = t), register r, picked with exact one-hot multiply-adds
+              float4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int m = 0; m < KM; ++m) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], kf[m], gram, 0, 0, 0);
+              const float dg = fmaf(gram[3], dsel3, fmaf(gram[2], dsel2, fmaf(gram[1], dsel1, gram[0] * dsel0)));
+              const int plane = static_cast<uint32_t>(diag_r) < 4u ? 3 : 4;
+              tokf[wave][plane][u][col] = dg;
+            }
+          }
+
+          // ---- phase B: per-token factors once, the scores of every row
+          // group in log2 units (-inf: masked) and their column maxima
+          wave_lds_sync();  // per-token scalars written by other lanes
+          float fk[2][4], bk[2][4];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float4_t fb4 = *reinterpret_cast<const float4_t *>(&tokf[wave][0][u][4 * kq]);
+            float4_t nn4 = {1.0f, 1.0f, 1.0f, 1.0f};
+            if (nc) nn4 = *reinterpret_cast<const float4_t *>(&tokf[wave][3][u][4 * kq]);
+            s1v[u] = *reinterpret_cast<const float4_t *>(&tokf[wave][1][u][4 * kq]);
+            zcv[u] = *reinterpret_cast<const float4_t *>(&tokf[wave][2][u][4 * kq]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float f = fb4[r];
+              // centroids carry the table scale sigma: it cancels under norm
+              // correction and is divided out otherwise
+              if constexpr (GE::kMse) f *= nc ? __builtin_amdgcn_rsqf(nn4[r]) : inv_sigma;
+              // live tokens: f >= 0 and bias 0; masked ones (fb = -inf):
+              // factor 0 and bias -inf (a Gram entry of 0 there gives
+              // -inf * inf = -inf)
+              fk[u][r] = fmax_raw(f, 0.0f);
+              bk[u][r] = fmin_raw(fb4[r], 0.0f);
+            }
+          }
+          wave_lds_sync();  // scalar reads done before the next pair rewrites them
+          bool grow = false;
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                // MSE scores are finite: masked ones become 0 * f + -inf. FP8
+                // codes of a masked tile may decode to NaN: select instead.
+                if constexpr (GE::kMse) sv[gi][u][r] = fmaf(sraw[gi][u][r], fk[u][r], bk[u][r]);
+                else sv[gi][u][r] = bk[u][r] == 0.0f ? sraw[gi][u][r] * fk[u][r] : -INFINITY;
+              }
+            const float mloc = fmaxf(fmaxf(fmaxf(sv[gi][0][0], sv[gi][0][1]), fmaxf(sv[gi][0][2], sv[gi][0][3])),
+                                     fmaxf(fmaxf(sv[gi][1][0], sv[gi][1][1]), fmaxf(sv[gi][1][2], sv[gi][1][3])));
+            mt[gi] = column_max_raw(mloc);
+            grow = grow || mt[gi] > m_run[gi] + kLazy;
+          }
+          if (lane_mask(grow) != 0ull) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) rescale(gi, mt[gi]);
+          }
+        }
+
+        // ---- phase C: the weights of every row group, the value codes of
+        // the pair expanded once, the value MFMAs of every row group
+        u32x4_t bh[NG], bl[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          const float mr = (m_run[gi] == -INFINITY) ? 0.0f : m_run[gi];
+          uint32_t hw[2][2], lw[2][2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float wv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float pr = __builtin_amdgcn_exp2f(sv[gi][u][r] - mr);
+              l_lane[gi] += pr;
+              z_lane[gi] = fmaf(pr, zcv[u][r], z_lane[gi]);
+              wv[r] = pr * s1v[u][r];
+            }
+            // weights p s' as f16 hi + lo parts: the value contraction sees
+            // them to ~21 bits
+            split_f16_pairs(wv, hw[u], lw[u]);
+          }
+          bh[gi] = u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
+          bl[gi] = u32x4_t{lw[0][0], lw[0][1], lw[1][0], lw[1][1]};
+        }
+        typename VX::Prep p0, p1;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t *tw = scr + (cur + u) * (GE::kTileBuf / 4);
+          uint32_t vr[4];
+          // lanes past the last element group read group kGroups - 1 and keep zeros
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vr[r] = lds_field16<VB>(tw, val_off_rd + r * S);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? vr[r] : 0u;
+          VX::prep(vr, u == 0 ? p0 : p1);
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const half8_t av = __builtin_shufflevector(VX::get(p0, c), VX::get(p1, c), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi) {
+            acc[gi][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, bh[gi]), acc[gi][c], 0, 0, 0);
+            acc[gi][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, bl[gi]), acc[gi][c], 0, 0, 0);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        cur ^= 2;
+      }
+    }
+  }
+
+  // accumulators from expanded-code units (2^pos(c) per element c) to plain
+  // units: exact power-of-two scales
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[gi][c] *= VX::inv_scale(c);
+
+  // ---- the chunk's exact tokens, causally: the last split of a row block,
+  // one row group at a time (the chunk is short next to the history)
+  if (s == p.splits - 1) {
+    // chunk tokens any row of this block sees: 0 .. t_hi - 1
+    const int t_hi = min(clen, (min(row0 + R, nrows) - 1) / G + 1);
+    const int64_t kv_row = static_cast<int64_t>(p.num_kv_heads) * D;  // elements per chunk token
+    const uint16_t *kbase = p.k_chunk + (static_cast<int64_t>(c0) * p.num_kv_heads + h) * D;
+    const uint16_t *vbase = p.v_chunk + (static_cast<int64_t>(c0) * p.num_kv_heads + h) * D;
+    const bool vcol = col < GE::kGroups;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int row = row0 + 16 * gi + col;
+      const bool live_row = row < nrows;
+      const int trow = live_row ? row / G : -1;  // chunk token of this lane's row (-1: no row)
+      // chunk tokens this group's rows see
+      const int g_hi = min(t_hi, (min(row0 + 16 * gi + 16, nrows) - 1) / G + 1);
+      if (row0 + 16 * gi >= nrows) continue;
+      // raw query rows as bf16 hi + lo B operands, loaded in place
+      bf16x8_t qh[KM], qo[KM];
+      {
+        const int t = live_row ? row / G : 0;
+        const int64_t e0 = (static_cast<int64_t>(c0 + t) * Hq + h * G + (live_row ? row - t * G : 0)) * D + kq * (D / 4);
+#pragma unroll
+        for (int m = 0; m < KM; ++m) {
+          float x[8];
+          load_q8(p.q, q_dtype, e0 + 8 * m, live_row, x);
+          split_bf16(x, qh[m], qo[m]);
+        }
+      }
+      for (int ct = 0; ct < g_hi; ct += 2 * kTile) {
+          float sv[2][4];
+          u32x4_t vv[8];
+          {
+            // keys of this lane's token (col) of both tiles, and the value
+            // vectors (element group col) of its 8 tokens: all loads in
+            // flight together
+            u32x4_t kraw[2][KM];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int tok = ct + u * kTile + col;
+              const bool live = tok < g_hi;
+              const u32x4_t *src = reinterpret_cast<const u32x4_t *>(kbase + (live ? tok : 0) * kv_row + kq * (D / 4));
+#pragma unroll
+              for (int m = 0; m < KM; ++m) kraw[u][m] = live ? src[m] : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int tok = ct + (e < 4 ? 4 * kq + e : kTile + 4 * kq + e - 4);
+              const bool live = vcol && tok < g_hi;
+              vv[e] = live ? *reinterpret_cast<const u32x4_t *>(vbase + tok * kv_row + 8 * col) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              float4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int m = 0; m < KM; ++m) {
+                const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kraw[u][m]);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qh[m], a, 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qo[m], a, 0, 0, 0);
+              }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int tok = ct + u * kTile + 4 * kq + r;
+                sv[u][r] = tok <= trow ? a[r] * p.scale_log2 : -INFINITY;
+              }
+            }
+            const float mloc = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+            const float mtc = column_max_raw(mloc);
+            if (lane_mask(mtc > m_run[gi] + kLazy) != 0ull) rescale(gi, mtc);
+          }
+          const float mr = (m_run[gi] == -INFINITY) ? 0.0f : m_run[gi];
+          float pw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pw[e] = __builtin_amdgcn_exp2f(sv[e >> 2][e & 3] - mr);
+            l_lane[gi] += pw[e];
+          }
+          bf16x8_t ph, pl;
+          split_bf16(pw, ph, pl);
+          // element c of the lane's 8 tokens, token pairs packed in 16-bit halves
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            u32x4_t a;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) a[k] = perm(vv[2 * k + 1][c >> 1], vv[2 * k][c >> 1], sel);
+            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+            acc[gi][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ph, acc[gi][c], 0, 0, 0);
+            acc[gi][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl, acc[gi][c], 0, 0, 0);
+          }
+      }
+    }
+  }
+
+  // ---- partials (m, l, acc + zero terms) of the live rows
+  const int64_t bh_rows = (static_cast<int64_t>(b) * p.num_kv_heads + h) * p.rows_pad;
+  const int ps = pstride(D);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const float l = column_sum(l_lane[gi]);
+    const float z = column_sum(z_lane[gi]);
+    const int row = row0 + 16 * gi + col;
+    if (row < nrows) {
+      float *dst = p.partials + ((bh_rows + row) * p.splits + s) * ps;
+      if (kq == 0) {
+        dst[0] = m_run[gi];
+        dst[1] = l;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int grp = 4 * kq + r;
+        if (grp < GE::kGroups) {
+          float4_t lo, hi;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            lo[c] = acc[gi][c][r] + z;
+            hi[c] = acc[gi][c + 4][r] + z;
+          }
+          *reinterpret_cast<float4_t *>(dst + kPad + 8 * grp) = lo;
+          *reinterpret_cast<float4_t *>(dst + kPad + 8 * grp + 4) = hi;
+        }
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge (base 2) of a row's split partials, normalised, to
+// out[cu[b] + t][h G + g]: D/4 threads per row, one float4 column each.
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_reduce_kernel(PrefillParams p) {
+  constexpr int kCols = D / 4;
+  constexpr int kRows = kThreads / kCols;
+  const int tid = threadIdx.x;
+  const int lr = tid / kCols;
+  const int c = tid - lr * kCols;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int row = blockIdx.x * kRows + lr;
+  const int G = p.group;
+  const int c0 = p.cu_chunk[b];
+  const int clen = min(max(p.cu_chunk[b + 1] - c0, 0), p.max_chunk);
+  if (lr >= kRows || row >= clen * G) return;
+  const int ps = pstride(D);
+  const float *part = p.partials + ((static_cast<int64_t>(b) * p.num_kv_heads + h) * p.rows_pad + row) * p.splits * ps;
+  float m = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, part[static_cast<int64_t>(s) * ps]);
+  float l = 0.0f;
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < p.splits; ++s) {
+    const float *e = part + static_cast<int64_t>(s) * ps;
+    const float ms = e[0];
+    if (ms > -INFINITY) {
+      const float wgt = exp2f(ms - m);
+      l = fmaf(e[1], wgt, l);
+      acc = acc + reinterpret_cast<const float4_t *>(e + kPad)[c] * wgt;
+    }
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const int t = row / G;
+  const int g = row - t * G;
+  reinterpret_cast<float4_t *>(p.out + (static_cast<int64_t>(c0 + t) * p.num_q_heads + h * G + g) * D)[c] = acc * inv;
+}
+
+template <int D, int KB, int VB, bool NC>
+int launch_t(tq_dtype q_dtype, const PrefillParams &p, hipStream_t st) {
+  const int qd = static_cast<int>(q_dtype);
+  const long long wgs = (static_cast<long long>(p.waves) + kWaves - 1) / kWaves;
+  if (wgs > 0) {
+    hipLaunchKernelGGL((prefill_attn_kernel<D, KB, VB, kPrefillRowGroups, NC>), dim3(static_cast<unsigned>(wgs)),
+                       dim3(64 * kWaves), 0, st, p, qd);
+    const int err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  constexpr int kRows = kThreads / (D / 4);
+  const unsigned gx = static_cast<unsigned>((p.rows_pad + kRows - 1) / kRows);
+  hipLaunchKernelGGL((prefill_reduce_kernel<D>), dim3(gx, p.num_kv_heads, p.batch), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int D, int KB, int VB>
+int launch_nc(tq_dtype qd, const PrefillParams &p, hipStream_t st, bool nc) {
+  if (KB != 8 && nc) return launch_t<D, KB, VB, KB != 8>(qd, p, st);
+  return launch_t<D, KB, VB, false>(qd, p, st);
+}
+
+template <int D>
+int launch_bits(const tq_config &c, tq_dtype qd, const PrefillParams &p, hipStream_t st) {
+  const int kb = c.key_quant_bits, vb = c.value_quant_bits;
+  const bool nc = c.norm_correction != 0;
+  if (kb == 3 && vb == 2) return launch_nc<D, 3, 2>(qd, p, st, nc);
+  if (kb == 4 && vb == 2) return launch_nc<D, 4, 2>(qd, p, st, nc);
+  if (kb == 8 && vb == 2) return launch_nc<D, 8, 2>(qd, p, st, nc);
+  if (kb == 3 && vb == 3) return launch_nc<D, 3, 3>(qd, p, st, nc);
+  if (kb == 3 && vb == 4) return launch_nc<D, 3, 4>(qd, p, st, nc);
+  if (kb == 4 && vb == 3) return launch_nc<D, 4, 3>(qd, p, st, nc);
+  if (kb == 4 && vb == 4) return launch_nc<D, 4, 4>(qd, p, st, nc);
+  if (kb == 8 && vb == 3) return launch_nc<D, 8, 3>(qd, p, st, nc);
+  if (kb == 8 && vb == 4) return launch_nc<D, 8, 4>(qd, p, st, nc);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int launch_prefill_prep(const PrefillParams &p, void *stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t qv = static_cast<int64_t>(p.vbatch) * p.num_kv_heads * 16 * p.head_dim * p.q_elem_bytes / 16;
-  hipLaunchKernelGGL(prefill_gather_q, dim3(grid_for(qv)), dim3(kThreads), 0, s, p);
-  const int64_t cv = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.max_chunk * (p.head_dim / 8);
-  hipLaunchKernelGGL(prefill_gather_chunk, dim3(grid_for(cv)), dim3(kThreads), 0, s, p);
-  hipLaunchKernelGGL(prefill_tables, dim3(p.vbatch), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
-}
-
-int launch_prefill_scatter(const PrefillParams &p, void *stream) {
-  const int64_t ov = static_cast<int64_t>(p.vbatch) * p.num_kv_heads * 16 * (p.head_dim / 4);
-  hipLaunchKernelGGL(prefill_scatter, dim3(grid_for(ov)), dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
-  return hipGetLastError();
+int launch_prefill(const tq_config &cfg, tq_dtype q_dtype, const PrefillParams &p, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (cfg.head_dim) {
+    case 64: return launch_bits<64>(cfg, q_dtype, p, st);
+    case 96: return launch_bits<96>(cfg, q_dtype, p, st);
+    case 128: return launch_bits<128>(cfg, q_dtype, p, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tq

@@ -248,9 +248,11 @@ tq_status tq_ring_append(const tq_config *cfg, const uint16_t *k_new, const uint
  *
  *   out[r, g, :] = sum_j softmax_j(scale * q[r, g] . k_j) v_j
  *
- * Query head g reads KV head g / (num_q_heads / num_kv_heads). The chunk
- * rows of one KV head are processed 16 at a time by the decode kernels, so
- * every 16 (token, head) rows stream the history once.
+ * Query head g reads KV head g / (num_q_heads / num_kv_heads). The (token,
+ * head) rows of one KV head are processed in blocks of 32: each history
+ * tile is decoded once per block and multiplied with all its rows, and the
+ * chunk's exact tokens are contracted on the matrix cores with the causal
+ * limit of each row.
  *
  *  q             device [N][num_q_heads][head_dim], dtype q_dtype, 16-byte
  *                aligned (N = cu_chunk[batch]).
@@ -260,11 +262,13 @@ tq_status tq_ring_append(const tq_config *cfg, const uint16_t *k_new, const uint
  *  hist_lens     device int32 [batch], at most max_hist (host bound).
  *  kv_pool, block_tables, block_size: as for tq_decode_attention.
  *  out           device fp32 [N][num_q_heads][head_dim], 16-byte aligned.
- *  workspace     device, tq_prefill_workspace_size bytes, 256-byte aligned;
- *                contents on entry do not matter.
- * batch * ceil(max_chunk * (num_q_heads / num_kv_heads) / 16) may be at most
- * 8192 (TQ_ERR_UNSUPPORTED otherwise: split the chunk). The chunk itself is
- * not written to the cache: tq_quantize_append does that.
+ *  workspace     device, tq_prefill_workspace_size bytes, 256-byte aligned
+ *                (one fp32 partial of head_dim + 4 floats per (row, history
+ *                split)); contents on entry do not matter.
+ * A history (max_hist > 0) needs num_blocks >= 1 (TQ_ERR_INVALID_ARG);
+ * max_chunk * (num_q_heads / num_kv_heads) must fit in 31 bits
+ * (TQ_ERR_UNSUPPORTED). The chunk itself is not written to the cache:
+ * tq_quantize_append does that.
  */
 tq_status tq_prefill_workspace_size(const tq_config *cfg, int batch, int num_q_heads, int num_kv_heads,
                                     int max_chunk, int max_hist, int max_blocks_per_seq,

@@ -212,6 +212,39 @@ def test_workspace_size_and_plan():
     assert b == 512 + -(-(975 * row) // 256) * 256
 
 
+def test_prefill_workspace_size_and_errors():
+    """One partial of D + 4 floats per (row, history split); rows padded to
+    blocks of 32 per KV head, splits chosen for about 2048 waves with at
+    least 1024 history tokens each."""
+    c = tq.config_from_preset("turboquant_4bit_nc", 128)
+    row = 132 * 4
+    # 4 sequences, 8 KV heads, 512-token chunks of 4 query heads per KV head:
+    # 2048 rows = 64 blocks per KV head, 2048 waves without a split
+    assert tq.prefill_workspace_size(c, 4, 32, 8, 512, 32768, 2048) == 4 * 8 * 2048 * row
+    # one sequence, 100-token chunk of 1 head: 4 blocks of 32 rows, 8 KV heads
+    # = 32 waves; 64 ranges wanted, 10000 // 1024 = 9 allowed, ceil(10000 / 9)
+    # -> 1120 tokens per range, 9 ranges
+    assert tq.prefill_workspace_size(c, 1, 8, 8, 100, 10000, 1000) == 8 * 128 * 9 * row
+    # no history: one split; 7 tokens x 8 heads = 56 rows, 2 blocks of 32
+    assert tq.prefill_workspace_size(c, 2, 16, 2, 7, 0, 0) == 2 * 2 * 64 * row
+    d96 = tq.config_from_preset("turboquant_k3v4_nc", 96)
+    assert tq.prefill_workspace_size(d96, 1, 16, 2, 9, 0, 0) == 2 * 96 * 100 * 4
+    buf = ctypes.create_string_buffer(4096 + 256)
+    al = (ctypes.addressof(buf) + 255) & ~255
+    cfgp = ctypes.byref(c)
+
+    def call(max_chunk=4, hq=8, hkv=2, nblocks=1, max_hist=16, ws=4096, bs=16):
+        return _c_call("tq_prefill_attention", cfgp, 0, al, tq.BF16, al, al, al, 1, max_chunk, hq, hkv, al, nblocks,
+                       bs, al, 1, al, max_hist, ctypes.c_float(0.0), al, al, ws, None)
+
+    assert call(hq=7) == 1                             # not a multiple of the KV heads
+    assert call(bs=24) == 3                            # block size not a multiple of 16
+    assert call(nblocks=0) == 1 and "one block" in tq.last_error()
+    assert call(max_chunk=1 << 30, hq=16, hkv=1) == 3  # rows beyond 31 bits
+    assert call(ws=16) == 4                            # workspace too small
+    assert call(max_chunk=0) == 0                      # nothing to do
+
+
 @pytest.mark.parametrize("num_layers", [0, 1, 2, 3, 4, 5, 10, 28, 32, 61])
 @pytest.mark.parametrize("n", [-1, 0, 1, 2, 3, 40])
 def test_boundary_skip_layers_match_oracle(num_layers, n):
