@@ -135,7 +135,7 @@ constexpr int64_t kPrefillTargetWaves = 2048;
 constexpr int64_t kPrefillMinSplitTokens = 1024;
 
 struct PrefillLayout {
-  int row_blocks = 0, rows_pad = 0, splits = 1, split_tokens = 32, waves = 0;
+  int row_blocks = 0, rows_pad = 0, row_quads = 0, splits = 1, split_tokens = 32, workgroups = 0;
   size_t total = 0;
 };
 
@@ -154,14 +154,16 @@ tq_status prefill_layout(const tq_config &cfg, int batch, int num_q_heads, int n
     split_tokens = ((max_hist + splits - 1) / splits + 31) / 32 * 32;
     splits = (max_hist + split_tokens - 1) / split_tokens;
   }
-  const int64_t waves = base * splits;
-  if (waves > INT32_MAX - 64)
+  const int64_t quads = (rb + 3) / 4;
+  const int64_t workgroups = static_cast<int64_t>(batch) * num_kv_heads * quads * splits;
+  if (workgroups > INT32_MAX / 4)
     return fail(TQ_ERR_UNSUPPORTED, "tq_prefill: too many (sequence, KV head, row block) work items; split the batch");
   L->row_blocks = static_cast<int>(rb);
   L->rows_pad = static_cast<int>(rb * kPrefillRows);
+  L->row_quads = static_cast<int>(quads);
   L->splits = static_cast<int>(splits);
   L->split_tokens = static_cast<int>(split_tokens);
-  L->waves = static_cast<int>(waves);
+  L->workgroups = static_cast<int>(workgroups);
   L->total = static_cast<size_t>(batch) * num_kv_heads * L->rows_pad * L->splits * (cfg.head_dim + 4) * sizeof(float);
   return TQ_OK;
 }
@@ -238,7 +240,8 @@ TQ_EXPORT tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx, co
   p.rows_pad = L.rows_pad;
   p.splits = L.splits;
   p.split_tokens = L.split_tokens;
-  p.waves = L.waves;
+  p.row_quads = L.row_quads;
+  p.workgroups = L.workgroups;
   const float scale = softmax_scale > 0.0f ? softmax_scale
                                            : static_cast<float>(1.0 / std::sqrt(static_cast<double>(cfg->head_dim)));
   p.scale_log2 = scale * 1.4426950408889634f;

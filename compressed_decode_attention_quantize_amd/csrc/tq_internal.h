@@ -113,7 +113,8 @@ struct DecodeParams {
 // Launchers (defined in the kernel translation units). Return hipSuccess or a
 // HIP error code as int.
 // Continuation prefill: one wave per (sequence, KV head, history split, row
-// block of 16 * kPrefillRowGroups query rows); rows of a KV head are ordered
+// block of 16 * kPrefillRowGroups query rows), four consecutive row blocks of
+// one (sequence, KV head, split) per workgroup; rows of a KV head are ordered
 // token-major (row r = t * group + g for query head h * group + g).
 constexpr int kPrefillRowGroups = 2;
 constexpr int kPrefillRows = 16 * kPrefillRowGroups;
@@ -141,7 +142,8 @@ struct PrefillParams {
   int32_t rows_pad;          // row_blocks * kPrefillRows
   int32_t splits;            // history ranges per row block
   int32_t split_tokens;      // tokens per history range (multiple of 32)
-  int32_t waves;             // batch * num_kv_heads * splits * row_blocks
+  int32_t row_quads;         // ceil(row_blocks / 4): workgroups per (sequence, KV head, split)
+  int32_t workgroups;        // batch * num_kv_heads * splits * row_quads
   float scale_log2;          // softmax scale * log2(e)
   float centroid_scale;      // sigma of the f16 centroid table
   uint32_t sign_words[4];

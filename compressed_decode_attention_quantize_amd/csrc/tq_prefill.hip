@@ -35,6 +35,8 @@
 //  reduce kernel (log-sum-exp merge of a row's split partials, written to
 //                out[token][query head]).
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 #include "tq_mfma.h"
@@ -110,22 +112,18 @@ __device__ __forceinline__ float column_max_raw(float v) {
   return fmax_raw(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-// f16 hi + lo parts of 4 weights (w0, w1 | w2, w3 packed pairs): hi rounded
-// toward zero, lo = w - hi rounded to f16 (|w - hi - lo| <= 2^-21 |w|). Each
-// residual is one mixed-precision multiply-add that reads its f16 half of hi
-// in place and writes its half of lo (v_fma_mixlo / v_fma_mixhi); the inputs
-// are ordinary VALU results.
-__device__ __forceinline__ void split_f16_pairs(const float w[4], uint32_t hw[2], uint32_t lw[2]) {
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    hw[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[2 * k], w[2 * k + 1]));
-    uint32_t lo;
-    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]\n\t"
-        "v_fma_mixhi_f16 %0, %3, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
-        : "=&v"(lo)
-        : "v"(w[2 * k]), "v"(hw[k]), "v"(w[2 * k + 1]));
-    lw[k] = lo;
-  }
+// f16 hi + lo parts of the products w0 = p0 s0, w1 = p1 s1 as packed pairs:
+// hi = RNE(p s), lo = RNE(fma(p, s, -hi)), so |w - hi - lo| <= 2^-22 |w|.
+// Mixed-precision multiply-adds form both halves from the f32 factors (the
+// product is never rounded to f32), reading hi's f16 halves in place; the
+// inputs are ordinary VALU results.
+__device__ __forceinline__ void split_prod_f16(float p0, float s0, float p1, float s1, uint32_t &hi, uint32_t &lo) {
+  asm("v_fma_mixlo_f16 %0, %2, %3, 0\n\t"
+      "v_fma_mixhi_f16 %0, %4, %5, 0\n\t"
+      "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(hi), "=&v"(lo)
+      : "v"(p0), "v"(s0), "v"(p1), "v"(s1));
 }
 
 template <int D, int KB, int VB, int NG, bool NC>
@@ -135,17 +133,26 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
   constexpr int S = GE::kSlot;
   constexpr int KM = GE::kKM;
   constexpr int R = 16 * NG;        // query rows of a wave
-  constexpr int kBufs = 4;          // two pairs of tiles
-  constexpr int kLoads = GE::kChunksPerLane;
+  constexpr int kSets = 3;          // staged tile pairs: decoding, loading, spare
   constexpr bool nc = GE::kMse && NC;
+  static_assert(GE::kTileChunks <= 64 * kWaves, "a tile is one load instruction per wave");
 
+  // The four waves of a workgroup take four consecutive row blocks of one
+  // (sequence, KV head, history split) and share the history: each tile pair
+  // is staged once for the workgroup and decoded once, split over the
+  // waves (waves 0 and 1: key operand, Gram diagonal and per-token scalars
+  // of tile 0 and 1; waves 2 and 3: value operands of elements 0..3 and
+  // 4..7 of every 8-element group), into double-buffered operand arrays that
+  // every wave then multiplies with its own rows. One barrier per pair.
   __shared__ uint32_t lut[GE::kLut];
-  __shared__ __align__(16) uint32_t stage[kWaves][GE::stage_bytes(kBufs) / 4];
-  // per-token scalars of the macro tile: norm * scale (< 0: masked), s', z' + c0 s', ||c||^2;
-  // plane 4 takes the writes of lanes that hold nothing for a plane
-  __shared__ __align__(16) float tokf[kWaves][5][2][16];
+  __shared__ __align__(16) uint32_t stage[kSets][2][GE::kTileBuf / 4];
+  __shared__ __align__(16) half8_t kop[2][2][KM][64];  // [parity][tile][k step][lane]
+  __shared__ __align__(16) half8_t vop[2][8][64];      // [parity][element c][lane]
+  // per-token scalars of a pair: score factor (-inf: masked), s', z' + c0 s';
+  // plane 3 takes the writes of lanes that hold nothing for a plane
+  __shared__ __align__(16) float tokf[2][4][2][16];
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int kq = lane >> 4;
@@ -156,17 +163,14 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
       lut[e] = f16_pair_bits(p.centroids[lo] * p.centroid_scale, p.centroids[hi] * p.centroid_scale);
     }
   }
-  __syncthreads();  // the last workgroup barrier; waves are independent below
 
-  // ---- work item. Logical workgroups follow each other on one XCD (the
-  // hardware deals workgroups to the 8 XCDs in turn), so the row blocks that
-  // stream the same history share that XCD's L2.
+  // ---- work item of the workgroup. Logical workgroups follow each other on
+  // one XCD (the hardware deals workgroups to the 8 XCDs in turn), so the
+  // row blocks that stream the same history share that XCD's L2.
   int wg = blockIdx.x;
   if ((gridDim.x & 7u) == 0) wg = (wg & 7) * static_cast<int>(gridDim.x >> 3) + (wg >> 3);
-  const int w = wg * kWaves + __builtin_amdgcn_readfirstlane(wave);
-  if (w >= p.waves) return;
-  const int rb = w % p.row_blocks;
-  int rest = w / p.row_blocks;
+  const int quad = wg % p.row_quads;
+  int rest = wg / p.row_quads;
   const int s = rest % p.splits;
   rest /= p.splits;
   const int h = rest % p.num_kv_heads;
@@ -175,19 +179,19 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
   const int Hq = p.num_q_heads;
   const int c0 = p.cu_chunk[b];
   const int clen = min(max(p.cu_chunk[b + 1] - c0, 0), p.max_chunk);
-  const int row0 = rb * R;
   const int nrows = clen * G;
-  if (row0 >= nrows) return;  // no live row: the reduce reads nothing of this block
+  // no live row in the workgroup: the reduce reads nothing of it
+  if (quad * kWaves * R >= nrows) return;
+  const int row0 = (quad * kWaves + wave) * R;  // this wave's rows (none: it still decodes its share)
   const int seq_cap = min(p.max_hist, p.max_blocks_per_seq * p.block_size);
   const int hist = min(max(p.hist_lens[b], 0), seq_cap);
   const int t_begin = min(hist, s * p.split_tokens);
   const int t_end = s == p.splits - 1 ? hist : min(hist, t_begin + p.split_tokens);
 
-  uint32_t *scr = stage[wave];  // this wave's LDS: queries, then the staged tiles
-
   // ---- rotated query rows as f16 hi + lo parts in the MFMA B-operand
-  // layout, one plane pass per row group: column n of group i is row
-  // row0 + 16 i + n (zero past the chunk).
+  // layout, one plane pass per row group through this wave's quarter of the
+  // key-operand array (free until the first pair is decoded, after a
+  // barrier): column n of group i is row row0 + 16 i + n (zero past the chunk).
   half8_t qf[NG][KM], ql[NG][KM];
   {
     using T = Team<D>;
@@ -195,7 +199,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
     const int r = lane - team * T::kLanes;
     constexpr int rows_per_pass = T::kPerWave;
     constexpr int kPasses = (16 + rows_per_pass - 1) / rows_per_pass;
-    _Float16 *qs = reinterpret_cast<_Float16 *>(scr);
+    static_assert(16 * D * 2 <= static_cast<int>(sizeof(kop)) / kWaves, "query plane fits a quarter of kop");
+    _Float16 *qs = reinterpret_cast<_Float16 *>(&kop[0][0][0][0]) + wave * (static_cast<int>(sizeof(kop)) / kWaves / 2);
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       u32x4_t qhi[kPasses], qlo[kPasses];
@@ -272,10 +277,12 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
     m_run[gi] = mn;
   };
 
-  // ---- history: tiles HBM -> LDS by direct loads (lane l of a load
-  // instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS window), in
-  // pairs of tiles, two pair buffers per wave: the next pair is in flight
-  // while this one is used.
+  // ---- history: tile pairs HBM -> LDS by direct loads (lane l of a load
+  // instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS window; wave w
+  // loads chunks 64 w .. 64 w + 63 of each tile), three staged pairs. In
+  // iteration j: pair j + 2 loads, pair j + 1 is decoded (each wave its
+  // share), pair j is multiplied from the operands decoded the iteration
+  // before.
   if (t_begin < t_end) {
     const int32_t *bt_row = p.block_tables + static_cast<int64_t>(b) * p.max_blocks_per_seq;
     int nx_blk = t_begin / p.block_size;
@@ -287,10 +294,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
     const uint32_t blk_stride = static_cast<uint32_t>(p.num_kv_heads * p.block_size * S);
     const uint8_t *head_base = p.pool + static_cast<int64_t>(h) * p.block_size * S;
     const uint32_t nblk = static_cast<uint32_t>(p.num_blocks < 0x7fffffff ? p.num_blocks : 0x7fffffff);
-    const uint32_t stage_base = lds_offset(stage[0]) + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wave)) *
-                                                           (GE::stage_bytes(kBufs) / 4 * 4);
+    const uint32_t stage_base = lds_offset(&stage[0][0][0]) + 1024u * static_cast<uint32_t>(wave);
     const uint8_t *src = head_base;  // the last tile's source
-    uint32_t tile_ok = 0;            // bit k: buffer k holds a tile of a valid block
+    uint32_t tile_ok = 0;            // bit 2 set + u: tile u of staged pair `set` is of a valid block
     // the block-id window covers the blocks of the next two tiles
     auto cover = [&]() __attribute__((always_inline)) {
       if (nx_blk - blk_base + 2 > 64) {
@@ -299,9 +305,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
         wait_vmcnt<0>();
       }
     };
-    // Loads the next tile into buffer bsel. A tile past the range reloads the
-    // last source, so every pair issues the same number of loads, and is
-    // masked.
+    // This wave's share of the next tile into tile slot bsel (= 2 set + u).
+    // A tile past the range reloads the last source and is masked.
     auto issue = [&](int bsel) __attribute__((always_inline)) {
       const bool live = nx_tok < t_end;
       const int phys = __builtin_amdgcn_readlane(blk_lane, min(nx_blk - blk_base, 63));
@@ -317,166 +322,80 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
       const bool wrap = nx_off == p.block_size;
       nx_blk += wrap ? 1 : 0;
       nx_off = wrap ? 0 : nx_off;
-      const uint32_t dst = stage_base + bsel * GE::kTileBuf;
-      wait_lds_reads();  // earlier reads of this buffer (or the query plane) have executed
-#pragma unroll
-      for (int k = 0; k < kLoads; ++k) {
-        const int c = lane + 64 * k;
-        if (c < GE::kTileChunks) load_lds_16s(src, static_cast<uint32_t>(16 * c), dst + 1024 * k);
-      }
+      const int c = 64 * wave + lane;
+      if (c < GE::kTileChunks)
+        load_lds_16s(src, static_cast<uint32_t>(16 * c), stage_base + static_cast<uint32_t>(bsel) * GE::kTileBuf);
     };
 
     const float c0f = static_cast<float>(VX::kC0);
     const float inv_sigma = 1.0f / p.centroid_scale;
-    const uint64_t m_kq0 = lane_mask(kq == 0), m_kq1 = lane_mask(kq == 1), m_kq3 = lane_mask(kq == 3);
+    const uint64_t m_kq0 = lane_mask(kq == 0), m_kq1 = lane_mask(kq == 1);
     const int diag_r = col - 4 * kq;
     const float dsel0 = diag_r == 0 ? 1.0f : 0.0f, dsel1 = diag_r == 1 ? 1.0f : 0.0f;
     const float dsel2 = diag_r == 2 ? 1.0f : 0.0f, dsel3 = diag_r == 3 ? 1.0f : 0.0f;
     const uint32_t val_off_rd = static_cast<uint32_t>(4 * kq * S + GE::kKeyBytes + VB * min(col, GE::kGroups - 1));
+    // LDS planes this lane writes per token (loop-invariant): its lane-row
+    // scalar, and under norm correction the factor if it holds the diagonal
+    const int plane_v = ((nc && kq == 0) || kq == 3) ? 3 : kq;
+    const int plane_g = static_cast<uint32_t>(diag_r) < 4u ? 0 : 3;
 
-    cover();
-    issue(0);
-    issue(1);
-    int cur = 0;
-    for (int pt = t_begin; pt < t_end; pt += 2 * kTile) {
-      float sv[NG][2][4], mt[NG];
-      float4_t s1v[2], zcv[2];
-      {
+    // This wave's share of the decode of the staged pair `set` (first token
+    // tok0) into operand buffer `par`.
+    auto decode_share = [&](int set, int tok0, int par) __attribute__((always_inline)) {
+      if (wave < 2) {
+        // key operand, per-token scalars and Gram diagonal of tile u = wave
+        const int u = wave;
+        const int bsel = 2 * set + u;
+        const uint32_t *tw = &stage[set][u][0];
+        const int ntok = min(max(t_end - (tok0 + u * kTile), 0), kTile);
+        const bool tile_valid = (tile_ok >> bsel) & 1u;
+        constexpr uint32_t kScaleOff = GE::kKeyBytes + GE::kValCodeBytes;
+        uint32_t x;
         {
-          const int nxt = cur ^ 2;
-          cover();
-          issue(nxt);
-          issue(nxt + 1);
-          wait_vmcnt<2 * kLoads>();  // this pair's loads are done, the next pair's may run
-
-          // ---- phase A, per tile: the key operand once, the scores of
-          // every row group, per-token scalars to LDS
-          float4_t sraw[NG][2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int bsel = cur + u;
-            const uint32_t *tw = scr + bsel * (GE::kTileBuf / 4);
-            const int ntok = min(max(t_end - (pt + u * kTile), 0), kTile);
-            const bool tile_valid = (tile_ok >> bsel) & 1u;
-            constexpr uint32_t kScaleOff = GE::kKeyBytes + GE::kValCodeBytes;
-            uint32_t x;
-            {
-              const uint16_t *hh = reinterpret_cast<const uint16_t *>(tw);
-              const uint32_t off = static_cast<uint32_t>(col * S) + (kq == 0 ? GE::kKeyCodeBytes : kScaleOff);
-              x = static_cast<uint32_t>(hh[off >> 1]) | (static_cast<uint32_t>(hh[(off >> 1) + 1]) << 16);
-            }
-            half8_t kf[KM];
-            key_operand<D, KB, VB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
-            {
-              // plane kq of token col: norm * scale (-inf: masked), s', z' + c0 s', 1
-              const float a = f16_bits_to_float(x & 0xffffu);
-              const float z1 = f16_bits_to_float(x >> 16);
-              const uint64_t ok = tile_valid ? column_mask(ntok) : 0ull;
-              const float fb = GE::kMse ? p.scale_log2 * a : p.scale_log2;
-              const float val_k = mask_select(ok, fb, -INFINITY);
-              const float val_v = mask_select(ok, mask_select(m_kq1, a, fmaf(c0f, a, z1)), 0.0f);
-              float val = mask_select(m_kq0, val_k, val_v);
-              val = mask_select(m_kq3, 1.0f, val);
-              tokf[wave][kq][u][col] = val;
-            }
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-              float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-              for (int m = 0; m < KM; ++m) {
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[gi][m], sc, 0, 0, 0);
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], ql[gi][m], sc, 0, 0, 0);
-              }
-              sraw[gi][u] = sc;
-            }
-            if constexpr (nc) {
-              // ||c_t||^2 of token t = 4kq + r on the Gram diagonal: lane (kq,
-              // col = t), register r, picked with exact one-hot multiply-adds
-              float4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-              for (int m = 0; m < KM; ++m) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], kf[m], gram, 0, 0, 0);
-              const float dg = fmaf(gram[3], dsel3, fmaf(gram[2], dsel2, fmaf(gram[1], dsel1, gram[0] * dsel0)));
-              const int plane = static_cast<uint32_t>(diag_r) < 4u ? 3 : 4;
-              tokf[wave][plane][u][col] = dg;
-            }
-          }
-
-          // ---- phase B: per-token factors once, the scores of every row
-          // group in log2 units (-inf: masked) and their column maxima
-          wave_lds_sync();  // per-token scalars written by other lanes
-          float fk[2][4], bk[2][4];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const float4_t fb4 = *reinterpret_cast<const float4_t *>(&tokf[wave][0][u][4 * kq]);
-            float4_t nn4 = {1.0f, 1.0f, 1.0f, 1.0f};
-            if (nc) nn4 = *reinterpret_cast<const float4_t *>(&tokf[wave][3][u][4 * kq]);
-            s1v[u] = *reinterpret_cast<const float4_t *>(&tokf[wave][1][u][4 * kq]);
-            zcv[u] = *reinterpret_cast<const float4_t *>(&tokf[wave][2][u][4 * kq]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float f = fb4[r];
-              // centroids carry the table scale sigma: it cancels under norm
-              // correction and is divided out otherwise
-              if constexpr (GE::kMse) f *= nc ? __builtin_amdgcn_rsqf(nn4[r]) : inv_sigma;
-              // live tokens: f >= 0 and bias 0; masked ones (fb = -inf):
-              // factor 0 and bias -inf (a Gram entry of 0 there gives
-              // -inf * inf = -inf)
-              fk[u][r] = fmax_raw(f, 0.0f);
-              bk[u][r] = fmin_raw(fb4[r], 0.0f);
-            }
-          }
-          wave_lds_sync();  // scalar reads done before the next pair rewrites them
-          bool grow = false;
-#pragma unroll
-          for (int gi = 0; gi < NG; ++gi) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                // MSE scores are finite: masked ones become 0 * f + -inf. FP8
-                // codes of a masked tile may decode to NaN: select instead.
-                if constexpr (GE::kMse) sv[gi][u][r] = fmaf(sraw[gi][u][r], fk[u][r], bk[u][r]);
-                else sv[gi][u][r] = bk[u][r] == 0.0f ? sraw[gi][u][r] * fk[u][r] : -INFINITY;
-              }
-            const float mloc = fmaxf(fmaxf(fmaxf(sv[gi][0][0], sv[gi][0][1]), fmaxf(sv[gi][0][2], sv[gi][0][3])),
-                                     fmaxf(fmaxf(sv[gi][1][0], sv[gi][1][1]), fmaxf(sv[gi][1][2], sv[gi][1][3])));
-            mt[gi] = column_max_raw(mloc);
-            grow = grow || mt[gi] > m_run[gi] + kLazy;
-          }
-          if (lane_mask(grow) != 0ull) {
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi) rescale(gi, mt[gi]);
-          }
+          const uint16_t *hh = reinterpret_cast<const uint16_t *>(tw);
+          const uint32_t off = static_cast<uint32_t>(col * S) + (kq == 0 ? GE::kKeyCodeBytes : kScaleOff);
+          x = static_cast<uint32_t>(hh[off >> 1]) | (static_cast<uint32_t>(hh[(off >> 1) + 1]) << 16);
         }
-
-        // ---- phase C: the weights of every row group, the value codes of
-        // the pair expanded once, the value MFMAs of every row group
-        u32x4_t bh[NG], bl[NG];
+        half8_t kf[KM];
+        key_operand<D, KB, VB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          const float mr = (m_run[gi] == -INFINITY) ? 0.0f : m_run[gi];
-          uint32_t hw[2][2], lw[2][2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float wv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float pr = __builtin_amdgcn_exp2f(sv[gi][u][r] - mr);
-              l_lane[gi] += pr;
-              z_lane[gi] = fmaf(pr, zcv[u][r], z_lane[gi]);
-              wv[r] = pr * s1v[u][r];
-            }
-            // weights p s' as f16 hi + lo parts: the value contraction sees
-            // them to ~21 bits
-            split_f16_pairs(wv, hw[u], lw[u]);
-          }
-          bh[gi] = u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
-          bl[gi] = u32x4_t{lw[0][0], lw[0][1], lw[1][0], lw[1][1]};
+        for (int m = 0; m < KM; ++m) kop[par][u][m][lane] = kf[m];
+        const uint64_t ok = tile_valid ? column_mask(ntok) : 0ull;  // live tokens
+        {
+          // plane kq of token col: the score factor (-inf: masked), s',
+          // z' + c0 s'. The factor is norm * scale / sigma (the centroids
+          // carry the table scale sigma), the constant scale for FP8 keys;
+          // under norm correction the lane holding the token's Gram diagonal
+          // writes it below instead.
+          const float a = f16_bits_to_float(x & 0xffffu);
+          const float z1 = f16_bits_to_float(x >> 16);
+          const float fb = GE::kMse ? p.scale_log2 * inv_sigma * a : p.scale_log2;
+          const float val_k = mask_select(ok, fb, -INFINITY);
+          const float val_v = mask_select(ok, mask_select(m_kq1, a, fmaf(c0f, a, z1)), 0.0f);
+          tokf[par][plane_v][u][col] = mask_select(m_kq0, val_k, val_v);
         }
+        if constexpr (nc) {
+          // ||c_t||^2 of token t = 4kq + r on the Gram diagonal: lane (kq,
+          // col = t), register r, picked with exact one-hot multiply-adds
+          float4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int m = 0; m < KM; ++m) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], kf[m], gram, 0, 0, 0);
+          const float dg = fmaf(gram[3], dsel3, fmaf(gram[2], dsel2, fmaf(gram[1], dsel1, gram[0] * dsel0)));
+          // the factor norm * scale / ||c||: sigma cancels; one reciprocal
+          // square root per token
+          const uint16_t *hh = reinterpret_cast<const uint16_t *>(tw);
+          const float nrm = f16_bits_to_float(hh[(static_cast<uint32_t>(col * S) + GE::kKeyCodeBytes) >> 1]);
+          const float fnc = p.scale_log2 * nrm * __builtin_amdgcn_rsqf(dg);
+          tokf[par][plane_g][u][col] = mask_select(ok, fnc, -INFINITY);
+        }
+      } else {
+        // value operands of elements c = 4 (wave - 2) .. + 3 of every group:
+        // tokens 4kq..4kq+3 of tile 0 in K slots 8kq..8kq+3, of tile 1 in
+        // 8kq+4..8kq+7
         typename VX::Prep p0, p1;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const uint32_t *tw = scr + (cur + u) * (GE::kTileBuf / 4);
+          const uint32_t *tw = &stage[set][u][0];
           uint32_t vr[4];
           // lanes past the last element group read group kGroups - 1 and keep zeros
 #pragma unroll
@@ -485,19 +404,151 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
           for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? vr[r] : 0u;
           VX::prep(vr, u == 0 ? p0 : p1);
         }
-        __builtin_amdgcn_s_setprio(1);
+        // elements at compile time keep the expansion's masks and offsets
+        // constant: one branch per wave half
+        auto emit = [&](auto half) __attribute__((always_inline)) {
+          constexpr int cb = 4 * decltype(half)::value;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const half8_t av = __builtin_shufflevector(VX::get(p0, c), VX::get(p1, c), 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int gi = 0; gi < NG; ++gi) {
-            acc[gi][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, bh[gi]), acc[gi][c], 0, 0, 0);
-            acc[gi][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, bl[gi]), acc[gi][c], 0, 0, 0);
-          }
-        }
-        __builtin_amdgcn_s_setprio(0);
-        cur ^= 2;
+          for (int k = 0; k < 4; ++k)
+            vop[par][cb + k][lane] =
+                __builtin_shufflevector(VX::get(p0, cb + k), VX::get(p1, cb + k), 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        if (wave == 2) emit(std::integral_constant<int, 0>{});
+        else emit(std::integral_constant<int, 1>{});
       }
+    };
+
+    // Scores, softmax weights and value MFMAs of the pair decoded into
+    // operand buffer `par` (first token tok0, staged pair `set`).
+    auto compute_pair = [&](int set, int tok0, int par) __attribute__((always_inline)) {
+      float4_t sraw[NG][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        half8_t kf[KM];
+#pragma unroll
+        for (int m = 0; m < KM; ++m) kf[m] = kop[par][u][m][lane];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          float4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int m = 0; m < KM; ++m) {
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], qf[gi][m], sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], ql[gi][m], sc, 0, 0, 0);
+          }
+          sraw[gi][u] = sc;
+        }
+      }
+      float4_t fb4[2], s1v[2], zcv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        fb4[u] = *reinterpret_cast<const float4_t *>(&tokf[par][0][u][4 * kq]);
+        s1v[u] = *reinterpret_cast<const float4_t *>(&tokf[par][1][u][4 * kq]);
+        zcv[u] = *reinterpret_cast<const float4_t *>(&tokf[par][2][u][4 * kq]);
+      }
+      // the exponent arguments s - m of every row group. Full pairs (both
+      // tiles inside the range, valid blocks): one fma per score with the
+      // reference maximum folded in, and a check that no column passes it by
+      // more than kLazy. Otherwise (a masked pair, or a column past the
+      // reference) the exact path: masked tokens at -inf, the rescale of the
+      // groups whose maximum grew.
+      float sv[NG][2][4];
+      const bool full = tok0 + 2 * kTile <= t_end && ((tile_ok >> (2 * set)) & 3u) == 3u;
+      bool grow = !full;
+      if (full) {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[gi][u][r] = fmaf(sraw[gi][u][r], fb4[u][r], -m_run[gi]);
+          const float mloc = fmaxf(fmaxf(fmaxf(sv[gi][0][0], sv[gi][0][1]), fmaxf(sv[gi][0][2], sv[gi][0][3])),
+                                   fmaxf(fmaxf(sv[gi][1][0], sv[gi][1][1]), fmaxf(sv[gi][1][2], sv[gi][1][3])));
+          grow = grow || column_max_raw(mloc) > kLazy;
+        }
+      }
+      if (lane_mask(grow) != 0ull) {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              // live tokens: factor >= 0, bias 0; masked ones (-inf): factor
+              // 0, bias -inf. MSE scores are finite; FP8 codes of a masked
+              // tile may decode to NaN: select instead.
+              const float f = fb4[u][r];
+              if constexpr (GE::kMse) sv[gi][u][r] = fmaf(sraw[gi][u][r], fmax_raw(f, 0.0f), fmin_raw(f, 0.0f));
+              else sv[gi][u][r] = f >= 0.0f ? sraw[gi][u][r] * f : -INFINITY;
+            }
+          const float mloc = fmaxf(fmaxf(fmaxf(sv[gi][0][0], sv[gi][0][1]), fmaxf(sv[gi][0][2], sv[gi][0][3])),
+                                   fmaxf(fmaxf(sv[gi][1][0], sv[gi][1][1]), fmaxf(sv[gi][1][2], sv[gi][1][3])));
+          const float mt = column_max_raw(mloc);
+          if (mt > m_run[gi] + kLazy || m_run[gi] == -INFINITY) rescale(gi, mt);
+          const float mr = (m_run[gi] == -INFINITY) ? 0.0f : m_run[gi];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[gi][u][r] -= mr;
+        }
+      }
+      // the weights p = exp2(s - m) of every row group, p s' as f16 hi + lo
+      // parts, then the value MFMAs of every row group
+      u32x4_t bh[NG], bl[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        uint32_t hw[2][2], lw[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float pr[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pr[r] = __builtin_amdgcn_exp2f(sv[gi][u][r]);
+            l_lane[gi] += pr[r];
+            z_lane[gi] = fmaf(pr[r], zcv[u][r], z_lane[gi]);
+          }
+          split_prod_f16(pr[0], s1v[u][0], pr[1], s1v[u][1], hw[u][0], lw[u][0]);
+          split_prod_f16(pr[2], s1v[u][2], pr[3], s1v[u][3], hw[u][1], lw[u][1]);
+        }
+        bh[gi] = u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
+        bl[gi] = u32x4_t{lw[0][0], lw[0][1], lw[1][0], lw[1][1]};
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const half8_t av = vop[par][c][lane];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          acc[gi][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, bh[gi]), acc[gi][c], 0, 0, 0);
+          acc[gi][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8_t, bl[gi]), acc[gi][c], 0, 0, 0);
+        }
+      }
+    };
+
+    // prologue: pairs 0 and 1 loading, pair 0 decoded
+    cover();
+    issue(0);
+    issue(1);
+    issue(2);
+    issue(3);
+    wait_vmcnt<0>();
+    __syncthreads();  // pair 0 staged; every wave's query plane reads done
+    decode_share(0, t_begin, 0);
+    int set_cur = 0, set_n1 = 1, set_n2 = 2, par = 0;
+    for (int pt = t_begin; pt < t_end; pt += 2 * kTile) {
+      wait_vmcnt<0>();  // this wave's loads of pair j + 1
+      // every wave's share of pair j + 1 has landed and its decode of pair j
+      // is in the operand buffers; the buffers the iteration rewrites were
+      // last read before this point
+      __syncthreads();
+      cover();
+      issue(2 * set_n2);
+      issue(2 * set_n2 + 1);
+      decode_share(set_n1, pt + 2 * kTile, par ^ 1);  // pair j + 1
+      compute_pair(set_cur, pt, par);                 // pair j
+      const int t = set_cur;
+      set_cur = set_n1;
+      set_n1 = set_n2;
+      set_n2 = t;
+      par ^= 1;
     }
   }
 
@@ -675,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void prefill_reduce_kernel(PrefillParams 
 template <int D, int KB, int VB, bool NC>
 int launch_t(tq_dtype q_dtype, const PrefillParams &p, hipStream_t st) {
   const int qd = static_cast<int>(q_dtype);
-  const long long wgs = (static_cast<long long>(p.waves) + kWaves - 1) / kWaves;
+  const long long wgs = p.workgroups;
   if (wgs > 0) {
     hipLaunchKernelGGL((prefill_attn_kernel<D, KB, VB, kPrefillRowGroups, NC>), dim3(static_cast<unsigned>(wgs)),
                        dim3(64 * kWaves), 0, st, p, qd);
