@@ -494,7 +494,7 @@ def run_prefill(args, w, tq, torch):
         "prefill": {"ms_mean": float(att_ms.mean()), "ms_p50": float(np.median(att_ms)), "flops": flops,
                     "TFLOPs": tflops},
         "append": {"ms_mean": float(app_ms.mean()), "tokens": n},
-        "roofline": {"bound": "mfma", "kernel": "tq_prefill_attention (layout + split + ring + reduce kernels)",
+        "roofline": {"bound": "mfma", "kernel": "tq_prefill_attention (attention + reduce kernels)",
                      "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None},
         "wall_s_timed": wall,

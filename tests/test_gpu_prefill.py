@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 from oracle import attention as OA
+from oracle import codec as OX
 from tests.gpu_common import ATTN_RTOL, announce, oracle_cfg, oracle_pool, per_head_rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -89,3 +90,55 @@ def test_prefill_garbage_workspace_and_repeat():
     assert np.isfinite(outs[0]).all()
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
     assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+
+
+@pytest.mark.timeout(900)
+def test_prefill_full_size_sampled():
+    """The continuation-prefill workload at full size (4 sequences x 32768
+    compressed history tokens + 512-token chunks, D=128, 32 q / 8 KV heads),
+    with the inputs and launch bench.py times: sampled rows (first, second,
+    middle and last chunk token of the first and last sequence, all query
+    heads) against the oracle's definition, row by row (the sequence's
+    dequantized history plus the chunk's exact tokens 0..t)."""
+    from workloads import WORKLOADS, KVSource
+    from workloads import gpu as WG
+
+    w = WORKLOADS["prefill_4bit_nc"]
+    picks = (0, w.batch - 1)
+    announce(f"prefill full size {w.name}: sequences {picks}")
+    built = WG.build(w, "cuda", n_pools=1, capture=picks, extra_blocks=w.batch * -(-w.chunk // w.block_size))
+    n = w.batch * w.chunk
+    ck, cv = KVSource(w, "cuda", stream_id=55).kv(n)
+    cq = KVSource(w, "cuda", stream_id=56).q(n)
+    cu = torch.arange(0, n + 1, w.chunk, dtype=torch.int32, device="cuda")
+    out = tq.prefill_attention(built.cfg, 0, cq, ck, cv, cu, w.chunk, built.pools[0], built.tables, built.seq_lens,
+                               built.max_seq_len)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ocfg = oracle_cfg(built.cfg)
+    q = cq.float().cpu().numpy()
+    kc = ck.float().cpu().numpy()
+    vc = cv.float().cpu().numpy()
+    bs = w.block_size
+    grp = w.num_q_heads // w.num_kv_heads
+    scale = 1.0 / math.sqrt(w.head_dim)
+    worst = 0.0
+    for b in picks:
+        kh_src, vh_src = built.captured[b]
+        m = kh_src.shape[0]
+        nblk = max(1, -(-m // bs))
+        opool = np.zeros((nblk, w.num_kv_heads, bs, ocfg.slot_size_aligned), np.uint8)
+        for s0 in range(0, m, 16384):
+            s1 = min(m, s0 + 16384)
+            OX.append(opool, kh_src[s0:s1], vh_src[s0:s1], np.arange(s0, s1), ocfg, 0)
+        table = np.arange(nblk, dtype=np.int32)
+        r0 = b * w.chunk
+        for h in range(w.num_kv_heads):
+            kh, vh = OA.sequence_kv(opool, table, m, h, ocfg, 0)
+            for t in (0, 1, w.chunk // 2, w.chunk - 1):
+                k = np.concatenate([kh, kc[r0:r0 + t + 1, h].astype(np.float64)], axis=0)
+                v = np.concatenate([vh, vc[r0:r0 + t + 1, h].astype(np.float64)], axis=0)
+                want = OA.softmax_attend(q[r0 + t, h * grp:(h + 1) * grp].astype(np.float64), k, v, scale)
+                worst = max(worst, per_head_rel_l2(got[r0 + t:r0 + t + 1, h * grp:(h + 1) * grp], want[None]))
+    announce(f"  sampled rows: max rel L2 {worst:.2e}")
+    assert worst <= ATTN_RTOL
