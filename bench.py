@@ -53,7 +53,7 @@ def kernel_source_sha():
     """Hash of the sources that decide a decode launch's traffic: the
     kernels and the host-side work plan (range lengths, partial slots)."""
     c = os.path.join(ROOT, "compressed_decode_attention_quantize_amd", "csrc")
-    return _sha([os.path.join(c, f) for f in ("tq_decode.hip", "tq_device.h", "tq_host.cpp", "tq_internal.h")])
+    return _sha([os.path.join(c, f) for f in ("tq_decode.hip", "tq_mfma.h", "tq_device.h", "tq_host.cpp", "tq_internal.h")])
 
 
 def _traffic(workload_name, per_launch_bytes):
