@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   uint64_t m_grp[NB];  // lanes of column group j
 #pragma unroll
   for (int j = 0; j < NB; ++j) m_grp[j] = lane_mask(my_tile == j);
-  const uint64_t m_kq0 = lane_mask(kq == 0), m_kq1 = lane_mask(kq == 1), m_kq3 = lane_mask(kq == 3);
+  const uint64_t m_kq0 = lane_mask(kq == 0), m_kq1 = lane_mask(kq == 1);
   // the Gram diagonal of token col sits in register col - 4 kq of lane row
   // kq: one-hot weights pick it with exact multiply-adds (the Gram entries
   // are finite). Ordinary arithmetic on purpose: an inline-asm select that
@@ -320,6 +320,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
   const int diag_r = col - 4 * kq;
   const float dsel0 = diag_r == 0 ? 1.0f : 0.0f, dsel1 = diag_r == 1 ? 1.0f : 0.0f;
   const float dsel2 = diag_r == 2 ? 1.0f : 0.0f, dsel3 = diag_r == 3 ? 1.0f : 0.0f;
+  // LDS planes this lane writes per token: its lane-row scalar, and under
+  // norm correction the score factor if it holds the token's Gram diagonal
+  constexpr bool kNcPlanes = GE::kMse && NC;
+  const int plane_v = ((kNcPlanes && kq == 0) || kq == 3) ? 4 : kq;
+  const int plane_g = static_cast<uint32_t>(diag_r) < 4u ? 0 : 4;
 
   // Tiles go HBM -> LDS by direct loads (global_load_lds_dwordx4: lane l of
   // a load instruction fills bytes [16 l, 16 l + 16) of a 1 KiB LDS window),
@@ -425,19 +430,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         half8_t kf[KM];
         key_operand<D, KB, VB>(tw, static_cast<uint32_t>(col * S + kq * GE::kLaneKeyBytes), lut, kf);
 
-        // per-token scalars of token col, plane kq: the norm times the
-        // softmax scale (negative marks a masked token), s', z' + c0 s', and
-        // 1 in plane 3 (the norm-correction pass overwrites it)
+        // per-token scalars of token col, plane kq: the score factor (-inf:
+        // masked), s', z' + c0 s'. The factor is norm * scale / sigma (the
+        // centroids carry the table scale sigma), the constant scale for FP8
+        // keys; under norm correction the lane holding the token's Gram
+        // diagonal writes it below instead (plane 4 takes unused writes).
+        const uint64_t ok = tile_ok ? column_mask(ntok) : 0ull;  // live tokens
         {
           const float a = f16_bits_to_float(x & 0xffffu);
           const float z1 = f16_bits_to_float(x >> 16);
-          const uint64_t ok = tile_ok ? column_mask(ntok) : 0ull;  // live tokens
-          const float fb = GE::kMse ? p.scale_log2 * a : p.scale_log2;
-          const float val_k = mask_select(ok, fb, -1.0f);
+          const float fb = GE::kMse ? p.scale_log2 * inv_sigma * a : p.scale_log2;
+          const float val_k = mask_select(ok, fb, -INFINITY);
           const float val_v = mask_select(ok, mask_select(m_kq1, a, fmaf(c0, a, z1)), 0.0f);
-          float val = mask_select(m_kq0, val_k, val_v);
-          val = mask_select(m_kq3, 1.0f, val);
-          tokf[wave][kq][i][col] = val;
+          tokf[wave][plane_v][i][col] = mask_select(m_kq0, val_k, val_v);
         }
 
         // keys -> scores S^T[4kq + r][col]; this lane keeps them if col is in
@@ -472,8 +477,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
             for (int m = 0; m < KM; ++m) gram = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[m], kf[m], gram, 0, 0, 0);
             const float dg = fmaf(gram[3], dsel3, fmaf(gram[2], dsel2, fmaf(gram[1], dsel1, gram[0] * dsel0)));
-            const int plane = static_cast<uint32_t>(diag_r) < 4u ? 3 : 4;
-            tokf[wave][plane][i][col] = dg;
+            // the factor norm * scale / ||c||: sigma cancels; one reciprocal
+            // square root per token
+            const uint16_t *hh = reinterpret_cast<const uint16_t *>(tw);
+            const float nrm = f16_bits_to_float(hh[(static_cast<uint32_t>(col * S) + GE::kKeyCodeBytes) >> 1]);
+            const float fnc = p.scale_log2 * nrm * __builtin_amdgcn_rsqf(dg);
+            tokf[wave][plane_g][i][col] = mask_select(ok, fnc, -INFINITY);
           }
         }
 
@@ -492,7 +501,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         // softmax still multiplies the slot's scale / zero by its zero
         // weights, so they must be finite: LDS holds whatever an earlier
         // workgroup left there (packed slot bytes can read as Inf or NaN)
-        tokf[wave][kq][i][col] = kq == 0 ? -1.0f : (kq == 3 ? 1.0f : 0.0f);
+        tokf[wave][kq][i][col] = kq == 0 ? -INFINITY : 0.0f;
         tbuf[i] = 0;
         if constexpr (!kValLds) {
 #pragma unroll
@@ -510,36 +519,38 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     for (int u = 0; u < TL; ++u) {
       const int ti = TL == 1 ? my_tile : u;
       const float4_t fb4 = *reinterpret_cast<const float4_t *>(&tokf[wave][0][ti][4 * kq]);
-      float4_t nn4 = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (nc) nn4 = *reinterpret_cast<const float4_t *>(&tokf[wave][3][ti][4 * kq]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float f = fb4[r];
-        if constexpr (GE::kMse) {
-          // centroids carry the table scale sigma: it cancels under norm
-          // correction and is divided out otherwise
-          f *= nc ? __builtin_amdgcn_rsqf(nn4[r]) : inv_sigma;
-        }
-        s[u][r] = (fb4[r] >= 0.0f) ? sraw[u][r] * f : -INFINITY;
+        // live tokens: factor >= 0, bias 0; masked ones (-inf): factor 0,
+        // bias -inf. MSE scores are finite; FP8 codes of a masked tile may
+        // decode to NaN: select instead.
+        const float f = fb4[r];
+        if constexpr (GE::kMse) s[u][r] = fmaf(sraw[u][r], fmax_raw(f, 0.0f), fmin_raw(f, 0.0f));
+        else s[u][r] = f >= 0.0f ? sraw[u][r] * f : -INFINITY;
       }
     }
     // running max of the column: the lane's registers, then the 4 lane rows
     float mloc = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
 #pragma unroll
     for (int u = 1; u < TL; ++u) mloc = fmaxf(mloc, fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3])));
-    float mt = column_max(mloc);
+    float mt = column_max_raw(mloc);
     if constexpr (kFold) {
       // one maximum per query head over all column groups
-      if constexpr (NB == 4) mt = fmaxf(mt, row_ror<4>(mt));
-      mt = fmaxf(mt, row_ror<8>(mt));
+      if constexpr (NB == 4) mt = fmax_raw(mt, row_ror<4>(mt));
+      mt = fmax_raw(mt, row_ror<8>(mt));
     }
-    if (mt > m_run) {
-      const float alpha = exp2f(m_run - mt);
+    // lazy reference maximum: weights are exp2(s - m_run), m_run moves only
+    // when a column's maximum passes it by more than kLazy (weights up to
+    // 2^kLazy; the normalisation by l cancels the reference), so the
+    // rescale of the accumulators is rare
+    if (mt > m_run + kLazy) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - mn);
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] *= alpha;
       l_lane *= alpha;
       z_lane *= alpha;
-      m_run = mt;
+      m_run = mn;
     }
     const float mr = (m_run == -INFINITY) ? 0.0f : m_run;
     // weights p * s' as f16 hi + lo parts: the value contraction then sees
@@ -551,20 +562,18 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
       const int ti = TL == 1 ? my_tile : u;
       const float4_t s14 = *reinterpret_cast<const float4_t *>(&tokf[wave][1][ti][4 * kq]);
       const float4_t zc4 = *reinterpret_cast<const float4_t *>(&tokf[wave][2][ti][4 * kq]);
-      float w[4];
+      float pr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(s[u][r] - mr);
-        l_lane += pr;
-        z_lane = fmaf(pr, zc4[r], z_lane);
-        w[r] = pr * s14[r];
+        pr[r] = __builtin_amdgcn_exp2f(s[u][r] - mr);
+        l_lane += pr[r];
+        z_lane = fmaf(pr[r], zc4[r], z_lane);
       }
-      hw[u][0] = f16_pair_bits(w[0], w[1]);
-      hw[u][1] = f16_pair_bits(w[2], w[3]);
-      lw[u][0] = f16_pair_bits(w[0] - f16_bits_to_float(hw[u][0] & 0xffffu),
-                               w[1] - f16_bits_to_float(hw[u][0] >> 16));
-      lw[u][1] = f16_pair_bits(w[2] - f16_bits_to_float(hw[u][1] & 0xffffu),
-                               w[3] - f16_bits_to_float(hw[u][1] >> 16));
+      uint32_t h0, l0, h1, l1;
+      split_prod_f16(pr[0], s14[0], pr[1], s14[1], h0, l0);
+      split_prod_f16(pr[2], s14[2], pr[3], s14[3], h1, l1);
+      hw[u] = u32x2_t{h0, h1};
+      lw[u] = u32x2_t{l0, l1};
     }
     wave_lds_sync();  // scalar reads done before the next macro tile rewrites them
 

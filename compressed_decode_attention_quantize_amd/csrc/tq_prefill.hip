@@ -49,7 +49,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kWaves = 4;       // waves per workgroup
 constexpr int kPad = 4;         // partial = [m, l, -, -, acc[D]]
 constexpr int kThreads = 256;   // reduce kernel
-constexpr float kLazy = 4.0f;   // reference-maximum slack of the online softmax (log2 units)
 
 __device__ __forceinline__ int pstride(int d) { return d + kPad; }
 
@@ -88,42 +87,6 @@ __device__ __forceinline__ void load_q8(const void *q, int q_dtype, int64_t e0, 
       }
     }
   }
-}
-
-// Plain v_max / v_min: the compiler puts a canonicalising max around
-// operands it cannot prove canonical (cross-lane moves, LDS reads); the
-// values here are finite or -inf. column_max_raw: maximum over the 4 lane
-// rows of an MFMA column (lanes c, c + 16, c + 32, c + 48) by the gfx950
-// row-swap permutes.
-__device__ __forceinline__ float fmax_raw(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float fmin_raw(float a, float b) {
-  float r;
-  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float column_max_raw(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmax_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmax_raw(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-
-// f16 hi + lo parts of the products w0 = p0 s0, w1 = p1 s1 as packed pairs:
-// hi = RNE(p s), lo = RNE(fma(p, s, -hi)), so |w - hi - lo| <= 2^-22 |w|.
-// Mixed-precision multiply-adds form both halves from the f32 factors (the
-// product is never rounded to f32), reading hi's f16 halves in place; the
-// inputs are ordinary VALU results.
-__device__ __forceinline__ void split_prod_f16(float p0, float s0, float p1, float s1, uint32_t &hi, uint32_t &lo) {
-  asm("v_fma_mixlo_f16 %0, %2, %3, 0\n\t"
-      "v_fma_mixhi_f16 %0, %4, %5, 0\n\t"
-      "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
-      : "=&v"(hi), "=&v"(lo)
-      : "v"(p0), "v"(s0), "v"(p1), "v"(s1));
 }
 
 template <int D, int KB, int VB, int NG, bool NC>
