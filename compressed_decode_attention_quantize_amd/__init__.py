@@ -24,7 +24,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtq.so")
+# TQ_LIBRARY names another build of the same library (the sanitizer build
+# of the host code that csrc/build.py --sanitize makes); default: the in-tree one
+LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(_HERE, "libtq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -64,10 +64,15 @@ typedef enum {
   TQ_ERR_UNKNOWN_PRESET = 2, /* tq_config_from_preset with an unknown name    */
   TQ_ERR_UNSUPPORTED = 3,    /* valid but not built (e.g. head_dim 256)       */
   TQ_ERR_WORKSPACE = 4,      /* decode workspace missing or too small         */
-  TQ_ERR_HIP = 5             /* a HIP launch or runtime call failed           */
+  TQ_ERR_HIP = 5,            /* a HIP launch or runtime call failed           */
+  TQ_STATUS_MAX_ENUM = 0x7fffffff /* no status: keeps the type a 32-bit integer */
 } tq_status;
 
-typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+/* Element types of query / key / value inputs. TQ_DTYPE_MAX_ENUM is no
+ * type: it keeps the enumeration a 32-bit integer whose every value is
+ * representable, so a caller's invalid value reaches the library's
+ * validation (TQ_ERR_INVALID_ARG) instead of being an out-of-range enum. */
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2, TQ_DTYPE_MAX_ENUM = 0x7fffffff } tq_dtype;
 
 /*
  * Configuration: the five dataclass fields of TurboQuantConfig ([API]) plus
