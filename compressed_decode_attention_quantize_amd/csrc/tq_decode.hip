@@ -926,13 +926,16 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
 }
 
 constexpr int kReduceThreads = 256;
-constexpr int kReduceBatch = 4;
+constexpr int kReduceBatch = 12;
 
 // Merge of the split partials of one (sequence, query head): nslots
 // compressed-token partials (+ the ring's). Thread (c, r) owns float4 column
 // c and merges slots r, r + R, ... with a running log-sum-exp (base 2),
-// kReduceBatch slots per step so their loads overlap; the R phases are then
-// merged through LDS.
+// kReduceBatch slots per step so their loads overlap. With R phases of
+// kReduceBatch slots, a segment of up to R kReduceBatch slots (120 at D = 96,
+// 96 at D = 128) is read in one round of loads, so the longest segment of a
+// ragged batch costs one memory round trip like the others. The phases are
+// then put on their common maximum and summed through LDS.
 template <int D>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeParams p) {
   constexpr int kCols = D / 4;                   // float4 columns
@@ -1003,27 +1006,31 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodePar
       }
     }
   }
-  __shared__ float4_t red_acc[kReduceThreads];
-  __shared__ float red_m[kReduceThreads], red_l[kReduceThreads];
-  red_m[tid] = m;
-  red_l[tid] = l;
-  red_acc[tid] = acc;
+  // phases -> their common maximum -> sum. Phases without a slot keep
+  // m = -inf and add nothing; with no slot at all the output is 0.
+  __shared__ float red_m[R], red_l[R];
+  __shared__ float4_t red_acc[R][kCols];
+  if (r < R && col == 0) red_m[r] = m;
+  __syncthreads();
+  if (r < R) {
+    float mm = -INFINITY;
+#pragma unroll 8
+    for (int i = 0; i < R; ++i) mm = fmaxf(mm, red_m[i]);
+    const float a = m > -INFINITY ? exp2f(m - mm) : 0.0f;
+    red_acc[r][col] = acc * a;
+    if (col == 0) red_l[r] = l * a;
+  }
   __syncthreads();
   if (r == 0) {
-    for (int rr = 1; rr < R; ++rr) {
-      const int t = rr * kCols + col;
-      const float ms = red_m[t];
-      if (ms > -INFINITY) {
-        const float mn = fmaxf(m, ms);
-        const float a = exp2f(m - mn);
-        const float w = exp2f(ms - mn);
-        acc = acc * a + red_acc[t] * w;
-        l = l * a + red_l[t] * w;
-        m = mn;
-      }
+    float4_t sum = red_acc[0][col];
+    float lsum = red_l[0];
+#pragma unroll 8
+    for (int i = 1; i < R; ++i) {
+      sum = sum + red_acc[i][col];
+      lsum += red_l[i];
     }
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    reinterpret_cast<float4_t *>(p.out + (static_cast<int64_t>(b) * p.num_q_heads + hq) * D)[col] = acc * inv;
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    reinterpret_cast<float4_t *>(p.out + (static_cast<int64_t>(b) * p.num_q_heads + hq) * D)[col] = sum * inv;
   }
 }
 
