@@ -11,22 +11,26 @@
 // Token t of sequence b's chunk attends to the sequence's compressed history
 // and, causally, to the chunk's exact bf16 tokens 0..t. The query rows of one
 // KV head are ordered token-major (row r = t * G + g for query head h G + g)
-// and cut into row blocks of R = 16 NG rows, one wave each: the wave decodes
-// every history tile once and multiplies it with its NG groups of 16 rows,
-// so a tile's key/value decode is shared by R rows instead of 16.
+// and cut into row blocks of R = 16 NG rows, one wave each, four consecutive
+// blocks to a workgroup: a history tile is decoded once per workgroup and
+// multiplied with all of its 4 R rows.
 //
-//  attention kernel (one wave per (sequence, KV head, history split, row block);
-//                four waves per workgroup sharing the code->f16 pair table)
-//     per 16-token history tile, staged HBM -> LDS one macro tile (two
-//     tiles) ahead:
-//       K~ = centroid values (MSE: pair table, FP8: hardware cvt), f16, once
+//  attention kernel (one workgroup of four waves per (sequence, KV head,
+//                history split, four consecutive 32-row blocks); each wave
+//                owns one row block, the decoded history is shared)
+//     per pair of 16-token history tiles, staged HBM -> LDS two pairs ahead
+//     by all four waves, then decoded once into LDS operand planes: waves 0
+//     and 1 each one tile's key operand, per-token scalars and Gram diagonal,
+//     waves 2 and 3 the pair's value operands (element groups 0-3 / 4-7):
+//       K~ = centroid values (MSE: pair table, FP8: hardware cvt), f16
+//       |c_t|^2 = diag(K~ K~^T)             (norm correction only)
+//     and every wave, for its own rows:
 //       S^T[t][row] = K~ . (Pi q)^T        MFMA 16x16x32 f16 per row group,
 //                                          q as f16 hi + lo parts
-//       |c_t|^2 = diag(K~ K~^T)             (norm correction only), once
 //       online softmax in exp2 per row group
 //       Out^T[j][row] += (code_tj - c0)^T . (p_t s'_t)   MFMA 16x16x32 f16
-//                      over tile pairs, codes expanded once per tile pair,
-//                      weights as f16 hi + lo parts per row group
+//                      over the tile pair, codes expanded by the 0x6400
+//                      exponent trick, weights as f16 hi + lo parts
 //       zero terms += p_t (z'_t + c0 s'_t)
 //     the last history split of a row block then takes the chunk's exact
 //     tokens 0..t (bf16 MFMA 16x16x32, raw q and the weights as bf16 hi + lo

@@ -208,8 +208,10 @@ def split_difference_bound(kappa, n):
     tokens (partials, merge). Under the probabilistic rounding model a sum
     of n terms errs by at most lambda sqrt(n) u of the sum of magnitudes
     (u = 2^-24), taken with lambda = 2 for each of the two runs. Relative
-    term errors e move the output by at most kappa e relative to its norm,
-    so the two runs differ by at most kappa (2 (2^-22 + 2^-23) + 4 sqrt(n) u)."""
+    term errors e move the output by at most kappa e relative to its norm
+    (kappa over the terms the kernel adds: centred codes times p s' and the
+    zero terms z' + c0 s' times p), so the two runs differ by at most
+    kappa (2 (2^-22 + 2^-23) + 4 sqrt(n) u)."""
     u = 2.0 ** -24
     return kappa * (2 * (2.0 ** -22 + 2.0 ** -23) + 4 * np.sqrt(n) * u)
 
