@@ -926,16 +926,16 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
 }
 
 constexpr int kReduceThreads = 256;
-constexpr int kReduceBatch = 12;
+constexpr int kReduceBatch = 6;
 
 // Merge of the split partials of one (sequence, query head): nslots
 // compressed-token partials (+ the ring's). Thread (c, r) owns float4 column
 // c and merges slots r, r + R, ... with a running log-sum-exp (base 2),
-// kReduceBatch slots per step so their loads overlap. With R phases of
-// kReduceBatch slots, a segment of up to R kReduceBatch slots (120 at D = 96,
-// 96 at D = 128) is read in one round of loads, so the longest segment of a
-// ragged batch costs one memory round trip like the others. The phases are
-// then put on their common maximum and summed through LDS.
+// kReduceBatch slots per step so their loads overlap: a segment of up to
+// R kReduceBatch slots (60 at D = 96, 48 at D = 128) is read in one round
+// of loads. Six keep the kernel within 64 VGPRs, so 8 waves per SIMD fit
+// and a 2048-workgroup grid runs in one generation. The phases are then put
+// on their common maximum and summed through LDS.
 template <int D>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeParams p) {
   constexpr int kCols = D / 4;                   // float4 columns
