@@ -154,7 +154,7 @@ tq_status prefill_layout(const tq_config &cfg, int batch, int num_q_heads, int n
     split_tokens = ((max_hist + splits - 1) / splits + 31) / 32 * 32;
     splits = (max_hist + split_tokens - 1) / split_tokens;
   }
-  const int64_t quads = (rb + 3) / 4;
+  const int64_t quads = (rb + kPrefillWaves - 1) / kPrefillWaves;
   const int64_t workgroups = static_cast<int64_t>(batch) * num_kv_heads * quads * splits;
   if (workgroups > INT32_MAX / 4)
     return fail(TQ_ERR_UNSUPPORTED, "tq_prefill: too many (sequence, KV head, row block) work items; split the batch");

@@ -113,10 +113,11 @@ struct DecodeParams {
 // Launchers (defined in the kernel translation units). Return hipSuccess or a
 // HIP error code as int.
 // Continuation prefill: one wave per (sequence, KV head, history split, row
-// block of 16 * kPrefillRowGroups query rows), four consecutive row blocks of
-// one (sequence, KV head, split) per workgroup; rows of a KV head are ordered
-// token-major (row r = t * group + g for query head h * group + g).
+// block of 16 * kPrefillRowGroups query rows), kPrefillWaves consecutive row
+// blocks of one (sequence, KV head, split) per workgroup; rows of a KV head
+// are ordered token-major (row r = t * group + g for query head h * group + g).
 constexpr int kPrefillRowGroups = 2;
+constexpr int kPrefillWaves = 8;
 constexpr int kPrefillRows = 16 * kPrefillRowGroups;
 struct PrefillParams {
   const void *q;             // [N][num_q_heads][D], q_dtype
@@ -142,7 +143,7 @@ struct PrefillParams {
   int32_t rows_pad;          // row_blocks * kPrefillRows
   int32_t splits;            // history ranges per row block
   int32_t split_tokens;      // tokens per history range (multiple of 32)
-  int32_t row_quads;         // ceil(row_blocks / 4): workgroups per (sequence, KV head, split)
+  int32_t row_quads;         // ceil(row_blocks / kPrefillWaves): workgroups per (sequence, KV head, split)
   int32_t workgroups;        // batch * num_kv_heads * splits * row_quads
   float scale_log2;          // softmax scale * log2(e)
   float centroid_scale;      // sigma of the f16 centroid table

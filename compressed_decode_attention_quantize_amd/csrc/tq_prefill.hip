@@ -50,7 +50,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = 4;       // waves per workgroup
+constexpr int kWaves = kPrefillWaves;  // waves per workgroup
 constexpr int kPad = 4;         // partial = [m, l, -, -, acc[D]]
 constexpr int kThreads = 256;   // reduce kernel
 
@@ -104,13 +104,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
   constexpr bool nc = GE::kMse && NC;
   static_assert(GE::kTileChunks <= 64 * kWaves, "a tile is one load instruction per wave");
 
-  // The four waves of a workgroup take four consecutive row blocks of one
+  // The kWaves waves of a workgroup take consecutive row blocks of one
   // (sequence, KV head, history split) and share the history: each tile pair
-  // is staged once for the workgroup and decoded once, split over the
-  // waves (waves 0 and 1: key operand, Gram diagonal and per-token scalars
-  // of tile 0 and 1; waves 2 and 3: value operands of elements 0..3 and
-  // 4..7 of every 8-element group), into double-buffered operand arrays that
-  // every wave then multiplies with its own rows. One barrier per pair.
+  // is staged once for the workgroup and decoded once, split over the first
+  // four waves (waves 0 and 1: key operand, Gram diagonal and per-token
+  // scalars of tile 0 and 1; waves 2 and 3: value operands of elements 0..3
+  // and 4..7 of every 8-element group), into double-buffered operand arrays
+  // that every wave then multiplies with its own rows. Waves 4 and up only
+  // multiply: two waves share a SIMD, so per pair a SIMD runs one decode
+  // share next to two waves' products. One barrier per pair.
   __shared__ uint32_t lut[GE::kLut];
   __shared__ __align__(16) uint32_t stage[kSets][2][GE::kTileBuf / 4];
   __shared__ __align__(16) half8_t kop[2][2][KM][64];  // [parity][tile][k step][lane]
@@ -156,9 +158,10 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
   const int t_end = s == p.splits - 1 ? hist : min(hist, t_begin + p.split_tokens);
 
   // ---- rotated query rows as f16 hi + lo parts in the MFMA B-operand
-  // layout, one plane pass per row group through this wave's quarter of the
-  // key-operand array (free until the first pair is decoded, after a
-  // barrier): column n of group i is row row0 + 16 i + n (zero past the chunk).
+  // layout, one plane pass per row group through a quarter of the key-operand
+  // array (waves 0-3) or of the value-operand array (waves 4-7), both free
+  // until the first pair is decoded, after a barrier: column n of group i is
+  // row row0 + 16 i + n (zero past the chunk).
   half8_t qf[NG][KM], ql[NG][KM];
   {
     using T = Team<D>;
@@ -166,8 +169,11 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
     const int r = lane - team * T::kLanes;
     constexpr int rows_per_pass = T::kPerWave;
     constexpr int kPasses = (16 + rows_per_pass - 1) / rows_per_pass;
-    static_assert(16 * D * 2 <= static_cast<int>(sizeof(kop)) / kWaves, "query plane fits a quarter of kop");
-    _Float16 *qs = reinterpret_cast<_Float16 *>(&kop[0][0][0][0]) + wave * (static_cast<int>(sizeof(kop)) / kWaves / 2);
+    static_assert(kWaves == 8, "query planes: four in kop, four in vop");
+    static_assert(16 * D * 2 <= static_cast<int>(sizeof(kop)) / 4, "query plane fits a quarter of kop");
+    static_assert(16 * D * 2 <= static_cast<int>(sizeof(vop)) / 4, "query plane fits a quarter of vop");
+    _Float16 *qs = wave < 4 ? reinterpret_cast<_Float16 *>(&kop[0][0][0][0]) + wave * (static_cast<int>(sizeof(kop)) / 8)
+                            : reinterpret_cast<_Float16 *>(&vop[0][0][0]) + (wave - 4) * (static_cast<int>(sizeof(vop)) / 8);
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       u32x4_t qhi[kPasses], qlo[kPasses];
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
           const float fnc = p.scale_log2 * nrm * __builtin_amdgcn_rsqf(dg);
           tokf[par][plane_g][u][col] = mask_select(ok, fnc, -INFINITY);
         }
-      } else {
+      } else if (wave < 4) {
         // value operands of elements c = 4 (wave - 2) .. + 3 of every group:
         // tokens 4kq..4kq+3 of tile 0 in K slots 8kq..8kq+3, of tile 1 in
         // 8kq+4..8kq+7
