@@ -254,10 +254,10 @@ tq_status tq_ring_append(const tq_config *cfg, const uint16_t *k_new, const uint
  *   out[r, g, :] = sum_j softmax_j(scale * q[r, g] . k_j) v_j
  *
  * Query head g reads KV head g / (num_q_heads / num_kv_heads). The (token,
- * head) rows of one KV head are processed in blocks of 32: each history
- * tile is decoded once per block and multiplied with all its rows, and the
- * chunk's exact tokens are contracted on the matrix cores with the causal
- * limit of each row.
+ * head) rows of one KV head are processed in blocks of 32, eight blocks to a
+ * workgroup: each history tile is decoded once per workgroup and multiplied
+ * with all of its rows, and the chunk's exact tokens are contracted on the
+ * matrix cores with the causal limit of each row.
  *
  *  q             device [N][num_q_heads][head_dim], dtype q_dtype, 16-byte
  *                aligned (N = cu_chunk[batch]).
