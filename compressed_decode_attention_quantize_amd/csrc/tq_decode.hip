@@ -585,13 +585,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         // the tile is still in its buffer: the next load went to the spare one
         const uint32_t *tw = scr + tbuf[i] * (GE::kTileBuf / 4);
         uint32_t vr[4];
-        // every lane reads (lanes past the last element group read group
-        // kGroups - 1, inside the tile, and keep zeros)
+        // every lane reads: lanes past the last element group (col >=
+        // kGroups, at D < 128) read group kGroups - 1, inside the tile. Those
+        // codes are finite, and they only reach output rows 8 col + c >= D of
+        // the value MFMAs, which are padding and never written out.
 #pragma unroll
         for (int r = 0; r < 4; ++r) vr[r] = lds_field16<VB>(tw, val_off_rd + r * S);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? vr[r] : 0u;
-        VX::prep(vr, pr);  // rows col >= kGroups are padding and never written out
+        VX::prep(vr, pr);
       } else {
         VX::prep(vraw[i], pr);
       }

@@ -370,11 +370,10 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
         for (int u = 0; u < 2; ++u) {
           const uint32_t *tw = &stage[set][u][0];
           uint32_t vr[4];
-          // lanes past the last element group read group kGroups - 1 and keep zeros
+          // lanes past the last element group (D < 128) read group kGroups - 1:
+          // finite codes that only reach the padding rows 8 col + c >= D
 #pragma unroll
           for (int r = 0; r < 4; ++r) vr[r] = lds_field16<VB>(tw, val_off_rd + r * S);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) vr[r] = col < GE::kGroups ? vr[r] : 0u;
           VX::prep(vr, u == 0 ? p0 : p1);
         }
         // elements at compile time keep the expansion's masks and offsets
