@@ -782,12 +782,9 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
   // this chunk's partial row (G query heads)
   float *prow = p.ring_partials + ((static_cast<int64_t>(b) * p.num_kv_heads + h) * p.ring_chunks + chunk) * G * pstride;
 
-  // A chunk that no query head sees (past the ring's length, or past every
-  // row's causal limit in a prefill chunk) gets the empty partial (m = -inf,
-  // l = 0, acc = 0) without loading anything.
-  bool live = tid < G && n > 0;
-  if (live && p.ring_row_lens) live = p.ring_row_lens[part0 + tid] > c0;
-  if (!__syncthreads_or(live)) {
+  // A chunk past the ring's length gets the empty partial (m = -inf, l = 0,
+  // acc = 0) without loading anything.
+  if (n == 0) {
     for (int e = tid; e < G * pstride; e += kRingThreads) {
       const int g = e / pstride, j = e - g * pstride;
       prow[static_cast<int64_t>(g) * pstride + j] = j == 0 ? -INFINITY : 0.0f;
@@ -795,8 +792,7 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
     return;
   }
 
-  const int rb = p.ring_group > 0 ? b / p.ring_group : b;  // the ring this sequence reads
-  const int64_t ring0 = ((static_cast<int64_t>(rb) * p.num_kv_heads + h) * p.ring_cap + c0) * D;
+  const int64_t ring0 = ((static_cast<int64_t>(b) * p.num_kv_heads + h) * p.ring_cap + c0) * D;
   float qv[kQLoads];
 #pragma unroll
   for (int i = 0; i < kQLoads; ++i) {
@@ -866,11 +862,7 @@ __global__ __launch_bounds__(kRingThreads) void decode_ring_kernel(DecodeParams 
 #pragma unroll
     for (int i = 0; i < kScoreHeads; ++i) {
       const int g = sg + kScoreGroups * i;
-      if (g < G) {
-        // a per-row limit (causal rows of a prefill chunk) cuts the chunk further
-        const int ng = p.ring_row_lens ? min(n, max(p.ring_row_lens[part0 + g] - c0, 0)) : n;
-        p_s[g][t] = t < ng ? dot[i] * p.scale_log2 : -INFINITY;
-      }
+      if (g < G) p_s[g][t] = t < n ? dot[i] * p.scale_log2 : -INFINITY;
     }
   }
   __syncthreads();

@@ -102,12 +102,6 @@ struct DecodeParams {
   float centroid_scale;    // sigma of the f16 centroid table
   uint32_t sign_words[4];
   float centroids[16];
-  // Shared rings (continuation prefill): sequences b .. b + ring_group - 1
-  // read ring b / ring_group (0: each sequence its own ring), and query head
-  // g of sequence b sees only ring tokens < ring_row_lens[b * Hq + g]
-  // (nullable: all of ring_lens[b]).
-  int32_t ring_group;
-  const int32_t *ring_row_lens;
 };
 
 // Launchers (defined in the kernel translation units). Return hipSuccess or a
