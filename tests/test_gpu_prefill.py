@@ -19,19 +19,24 @@ tq = pytest.importorskip("compressed_decode_attention_quantize_amd")
 DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 CASES = {
-    # name: (d, kb, vb, nc, hq, hkv, hist_lens, chunk_lens, q dtype)
+    # name: (d, kb, vb, nc, hq, hkv, hist_lens, chunk_lens, q dtype[, block size])
     "4bit_nc_g4": (128, 4, 4, True, 8, 2, [300, 0], [37, 5], "bf16"),
     "k3v4_d96_g8": (96, 3, 4, True, 16, 2, [1500, 17], [64, 1], "bf16"),
     "k8v2_d64_g1": (64, 8, 2, False, 2, 2, [40], [100], "f32"),
     "3bit_g16_f16": (128, 3, 3, True, 32, 2, [700, 129, 0], [9, 16, 33], "f16"),
+    # 48-token blocks: the history walk wraps blocks at offsets that are not
+    # powers of two
+    "4bit_bs48": (128, 4, 4, True, 8, 2, [700, 130], [20, 3], "bf16", 48),
+    # 5000 history tokens with few rows: four history splits of 1280 tokens,
+    # the last one ragged (1160)
+    "3bit_splits": (128, 3, 4, True, 8, 2, [5000], [40], "bf16"),
 }
 
 
-def _scenario(d, kb, vb, nc, hq, hkv, hist, chunks, qdt, seed):
+def _scenario(d, kb, vb, nc, hq, hkv, hist, chunks, qdt, seed, bs=16):
     cfg = tq.config_init(d, kb, vb, nc, 42)
     ocfg = oracle_cfg(cfg)
     rng = np.random.default_rng(seed)
-    bs = 16
     B = len(hist)
     nblk = [max(1, math.ceil(n / bs)) for n in hist]
     nb = sum(nblk) + 1
@@ -62,9 +67,9 @@ def _scenario(d, kb, vb, nc, hq, hkv, hist, chunks, qdt, seed):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_prefill_matches_oracle(name):
-    d, kb, vb, nc, hq, hkv, hist, chunks, qdt = CASES[name]
+    d, kb, vb, nc, hq, hkv, hist, chunks, qdt, *bs = CASES[name]
     announce(f"prefill {name}")
-    cfg, ocfg, pool, tables, cu, q, kc, vc = _scenario(d, kb, vb, nc, hq, hkv, hist, chunks, qdt, sum(name.encode()))
+    cfg, ocfg, pool, tables, cu, q, kc, vc = _scenario(d, kb, vb, nc, hq, hkv, hist, chunks, qdt, sum(name.encode()), *bs)
     out = tq.prefill_attention(cfg, 0, q.cuda(), kc.cuda(), vc.cuda(), torch.from_numpy(cu).cuda(), max(chunks),
                                torch.from_numpy(pool).cuda(), torch.from_numpy(tables).cuda(),
                                torch.tensor(hist, dtype=torch.int32).cuda(), max(hist))
@@ -77,7 +82,7 @@ def test_prefill_matches_oracle(name):
 
 def test_prefill_garbage_workspace_and_repeat():
     """Workspace contents on entry do not matter; repeated calls agree bit for bit."""
-    d, kb, vb, nc, hq, hkv, hist, chunks, qdt = CASES["4bit_nc_g4"]
+    d, kb, vb, nc, hq, hkv, hist, chunks, qdt, *_ = CASES["4bit_nc_g4"]
     announce("prefill garbage workspace")
     cfg, ocfg, pool, tables, cu, q, kc, vc = _scenario(d, kb, vb, nc, hq, hkv, hist, chunks, qdt, 5)
     args = (q.cuda(), kc.cuda(), vc.cuda(), torch.from_numpy(cu).cuda(), max(chunks), torch.from_numpy(pool).cuda(),
