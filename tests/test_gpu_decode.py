@@ -311,3 +311,34 @@ def test_ring_only():
     cfg, ocfg, pool_np, tables, q, ring = _scenario(128, 3, 3, True, 16, 2, lens, [128, 77], 128, seed=8)
     got, want = _run(cfg, ocfg, pool_np, tables, lens, q, ring)
     assert per_head_rel_l2(got, want) <= ATTN_RTOL
+
+
+def test_invalid_block_ids_skip_their_tokens():
+    """Block-table entries outside the pool (past num_blocks, or negative)
+    make the kernel read none of their slots: their tokens are masked. The
+    output is attention over the other tokens (the plain definition with
+    those positions removed), finite, with no fault."""
+    announce("decode invalid block ids")
+    lens = [700, 300]
+    cfg, ocfg, pool_np, tables, q, _ = _scenario(128, 4, 4, True, 8, 2, lens, seed=31)
+    nb, hkv, bs = pool_np.shape[0], pool_np.shape[1], pool_np.shape[2]
+    bad = tables.copy()
+    bad[0, 3] = nb + 7   # past the pool
+    bad[1, 0] = -1       # negative
+    drop = {0: {3}, 1: {0}}  # logical blocks whose tokens are skipped
+    out = tq.decode_attention(cfg, 0, q.cuda(), torch.from_numpy(pool_np).cuda(), torch.from_numpy(bad).cuda(),
+                              torch.tensor(lens, dtype=torch.int32).cuda(), max(lens))
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    qf = q.float().numpy().astype(np.float64)
+    g = q.shape[1] // hkv
+    want = np.zeros(got.shape, np.float64)
+    for b, n in enumerate(lens):
+        keep = np.array([(t // bs) not in drop[b] for t in range(n)], bool)
+        for h in range(hkv):
+            k, v = OA.sequence_kv(pool_np, tables[b], n, h, ocfg, 0)
+            want[b, h * g:(h + 1) * g] = OA.softmax_attend(qf[b, h * g:(h + 1) * g], k[keep], v[keep],
+                                                           1.0 / math.sqrt(q.shape[2]))
+    err = per_head_rel_l2(got, want)
+    announce(f"  rel L2 {err:.2e}")
+    assert err <= ATTN_RTOL

@@ -147,3 +147,40 @@ def test_prefill_full_size_sampled():
                 worst = max(worst, per_head_rel_l2(got[r0 + t:r0 + t + 1, h * grp:(h + 1) * grp], want[None]))
     announce(f"  sampled rows: max rel L2 {worst:.2e}")
     assert worst <= ATTN_RTOL
+
+
+def test_prefill_invalid_block_ids_skip_their_tokens():
+    """History blocks outside the pool (past num_blocks, or negative) are
+    read as nothing: their tokens are masked for every row, and each row
+    attends to the rest of the history plus its causal chunk tokens."""
+    announce("prefill invalid block ids")
+    hist, chunks = [300, 70], [10, 5]
+    cfg, ocfg, pool, tables, cu, q, kc, vc = _scenario(128, 4, 4, True, 8, 2, hist, chunks, "bf16", 44)
+    nb, hkv, bs = pool.shape[0], pool.shape[1], pool.shape[2]
+    bad = tables.copy()
+    bad[0, 2] = nb + 3   # past the pool
+    bad[1, 1] = -5       # negative
+    drop = {0: {2}, 1: {1}}
+    out = tq.prefill_attention(cfg, 0, q.cuda(), kc.cuda(), vc.cuda(), torch.from_numpy(cu).cuda(), max(chunks),
+                               torch.from_numpy(pool).cuda(), torch.from_numpy(bad).cuda(),
+                               torch.tensor(hist, dtype=torch.int32).cuda(), max(hist))
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    qf = q.float().numpy().astype(np.float64)
+    kcf = kc.float().numpy().astype(np.float64)
+    vcf = vc.float().numpy().astype(np.float64)
+    g = q.shape[1] // hkv
+    want = np.zeros(got.shape, np.float64)
+    for b in range(len(hist)):
+        keep = np.array([(t // bs) not in drop[b] for t in range(hist[b])], bool)
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        for h in range(hkv):
+            kh, vh = OA.sequence_kv(pool, tables[b], hist[b], h, ocfg, 0)
+            for t in range(r1 - r0):
+                k = np.concatenate([kh[keep], kcf[r0:r0 + t + 1, h]])
+                v = np.concatenate([vh[keep], vcf[r0:r0 + t + 1, h]])
+                want[r0 + t, h * g:(h + 1) * g] = OA.softmax_attend(qf[r0 + t, h * g:(h + 1) * g], k, v,
+                                                                    1.0 / math.sqrt(q.shape[2]))
+    err = per_head_rel_l2(got, want)
+    announce(f"  rel L2 {err:.2e}")
+    assert err <= ATTN_RTOL
