@@ -135,7 +135,7 @@ constexpr int64_t kPrefillTargetWaves = 2048;
 constexpr int64_t kPrefillMinSplitTokens = 1024;
 
 struct PrefillLayout {
-  int row_blocks = 0, rows_pad = 0, row_quads = 0, splits = 1, split_tokens = 32, workgroups = 0;
+  int row_blocks = 0, rows_pad = 0, row_sets = 0, splits = 1, split_tokens = 32, workgroups = 0;
   size_t total = 0;
 };
 
@@ -154,13 +154,13 @@ tq_status prefill_layout(const tq_config &cfg, int batch, int num_q_heads, int n
     split_tokens = ((max_hist + splits - 1) / splits + 31) / 32 * 32;
     splits = (max_hist + split_tokens - 1) / split_tokens;
   }
-  const int64_t quads = (rb + kPrefillWaves - 1) / kPrefillWaves;
-  const int64_t workgroups = static_cast<int64_t>(batch) * num_kv_heads * quads * splits;
+  const int64_t sets = (rb + kPrefillWaves - 1) / kPrefillWaves;
+  const int64_t workgroups = static_cast<int64_t>(batch) * num_kv_heads * sets * splits;
   if (workgroups > INT32_MAX / 4)
     return fail(TQ_ERR_UNSUPPORTED, "tq_prefill: too many (sequence, KV head, row block) work items; split the batch");
   L->row_blocks = static_cast<int>(rb);
   L->rows_pad = static_cast<int>(rb * kPrefillRows);
-  L->row_quads = static_cast<int>(quads);
+  L->row_sets = static_cast<int>(sets);
   L->splits = static_cast<int>(splits);
   L->split_tokens = static_cast<int>(split_tokens);
   L->workgroups = static_cast<int>(workgroups);
@@ -240,7 +240,7 @@ TQ_EXPORT tq_status tq_prefill_attention(const tq_config *cfg, int layer_idx, co
   p.rows_pad = L.rows_pad;
   p.splits = L.splits;
   p.split_tokens = L.split_tokens;
-  p.row_quads = L.row_quads;
+  p.row_sets = L.row_sets;
   p.workgroups = L.workgroups;
   const float scale = softmax_scale > 0.0f ? softmax_scale
                                            : static_cast<float>(1.0 / std::sqrt(static_cast<double>(cfg->head_dim)));

@@ -137,8 +137,8 @@ struct PrefillParams {
   int32_t rows_pad;          // row_blocks * kPrefillRows
   int32_t splits;            // history ranges per row block
   int32_t split_tokens;      // tokens per history range (multiple of 32)
-  int32_t row_quads;         // ceil(row_blocks / kPrefillWaves): workgroups per (sequence, KV head, split)
-  int32_t workgroups;        // batch * num_kv_heads * splits * row_quads
+  int32_t row_sets;          // ceil(row_blocks / kPrefillWaves): workgroups per (sequence, KV head, split)
+  int32_t workgroups;        // batch * num_kv_heads * splits * row_sets
   float scale_log2;          // softmax scale * log2(e)
   float centroid_scale;      // sigma of the f16 centroid table
   uint32_t sign_words[4];

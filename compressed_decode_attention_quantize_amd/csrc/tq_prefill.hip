@@ -11,17 +11,18 @@
 // Token t of sequence b's chunk attends to the sequence's compressed history
 // and, causally, to the chunk's exact bf16 tokens 0..t. The query rows of one
 // KV head are ordered token-major (row r = t * G + g for query head h G + g)
-// and cut into row blocks of R = 16 NG rows, one wave each, four consecutive
+// and cut into row blocks of R = 16 NG rows, one wave each, eight consecutive
 // blocks to a workgroup: a history tile is decoded once per workgroup and
-// multiplied with all of its 4 R rows.
+// multiplied with all of its 8 R rows.
 //
-//  attention kernel (one workgroup of four waves per (sequence, KV head,
-//                history split, four consecutive 32-row blocks); each wave
+//  attention kernel (one workgroup of eight waves per (sequence, KV head,
+//                history split, eight consecutive 32-row blocks); each wave
 //                owns one row block, the decoded history is shared)
 //     per pair of 16-token history tiles, staged HBM -> LDS two pairs ahead
-//     by all four waves, then decoded once into LDS operand planes: waves 0
-//     and 1 each one tile's key operand, per-token scalars and Gram diagonal,
-//     waves 2 and 3 the pair's value operands (element groups 0-3 / 4-7):
+//     by the waves, then decoded once into LDS operand planes: waves 0 and
+//     1 each one tile's key operand, per-token scalars and Gram diagonal,
+//     waves 2 and 3 the pair's value operands (element groups 0-3 / 4-7),
+//     waves 4-7 nothing:
 //       K~ = centroid values (MSE: pair table, FP8: hardware cvt), f16
 //       |c_t|^2 = diag(K~ K~^T)             (norm correction only)
 //     and every wave, for its own rows:
@@ -138,8 +139,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
   // row blocks that stream the same history share that XCD's L2.
   int wg = blockIdx.x;
   if ((gridDim.x & 7u) == 0) wg = (wg & 7) * static_cast<int>(gridDim.x >> 3) + (wg >> 3);
-  const int quad = wg % p.row_quads;
-  int rest = wg / p.row_quads;
+  const int rset = wg % p.row_sets;  // which kWaves consecutive row blocks
+  int rest = wg / p.row_sets;
   const int s = rest % p.splits;
   rest /= p.splits;
   const int h = rest % p.num_kv_heads;
@@ -150,8 +151,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillParams
   const int clen = min(max(p.cu_chunk[b + 1] - c0, 0), p.max_chunk);
   const int nrows = clen * G;
   // no live row in the workgroup: the reduce reads nothing of it
-  if (quad * kWaves * R >= nrows) return;
-  const int row0 = (quad * kWaves + wave) * R;  // this wave's rows (none: it still decodes its share)
+  if (rset * kWaves * R >= nrows) return;
+  const int row0 = (rset * kWaves + wave) * R;  // this wave's rows (none: it still decodes its share)
   const int seq_cap = min(p.max_hist, p.max_blocks_per_seq * p.block_size);
   const int hist = min(max(p.hist_lens[b], 0), seq_cap);
   const int t_begin = min(hist, s * p.split_tokens);
