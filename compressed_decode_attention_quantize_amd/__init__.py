@@ -55,6 +55,7 @@ if len(_hip_runtimes_loaded()) > 1:
                       "; import torch before any other HIP library")
 
 TQ_OK = 0
+TQ_ERR_INVALID_ARG = 1
 STATUS_NAMES = {0: "TQ_OK", 1: "TQ_ERR_INVALID_ARG", 2: "TQ_ERR_UNKNOWN_PRESET",
                 3: "TQ_ERR_UNSUPPORTED", 4: "TQ_ERR_WORKSPACE", 5: "TQ_ERR_HIP"}
 F32, BF16, F16 = 0, 1, 2
@@ -63,7 +64,8 @@ EXPORTED = ["tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_bo
             "tq_attn_page_size_1_token", "tq_slot_size", "tq_page_size",
             "tq_layer_signs", "tq_quantize_append", "tq_ring_flush", "tq_ring_append", "tq_decode_workspace_size",
             "tq_prefill_workspace_size", "tq_prefill_attention",
-            "tq_decode_attention", "tq_decode_attention_no_alloc", "tq_dequant", "tq_last_error", "tq_version"]
+            "tq_decode_attention", "tq_decode_attention_no_alloc", "tq_dequant", "tq_check_slot_mapping",
+            "tq_check_block_tables", "tq_last_error", "tq_version"]
 
 
 class Config(ctypes.Structure):
@@ -132,9 +134,13 @@ _lib.tq_decode_attention_no_alloc.argtypes = [_CP, ctypes.c_int, _P, ctypes.c_in
                                               ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P,
                                               ctypes.c_int, _P]
 _lib.tq_dequant.argtypes = [_CP, ctypes.c_int, _P, _i64, ctypes.c_int, ctypes.c_int, _P, _i64, _P, _P, _P]
+_lib.tq_check_slot_mapping.argtypes = [_P, _i64, _i64, ctypes.c_int, ctypes.POINTER(_i64)]
+_lib.tq_check_block_tables.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, _i64, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
 for _name in ("tq_config_init", "tq_config_from_preset", "tq_layer_config", "tq_layer_signs", "tq_quantize_append",
               "tq_ring_flush", "tq_ring_append", "tq_prefill_workspace_size", "tq_prefill_attention",
-              "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_attention_no_alloc", "tq_dequant"):
+              "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_attention_no_alloc", "tq_dequant",
+              "tq_check_slot_mapping", "tq_check_block_tables"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.tq_last_error.restype = ctypes.c_char_p
 _lib.tq_version.restype = ctypes.c_char_p
@@ -513,6 +519,48 @@ def dequant(cfg: Config, layer_idx: int, kv_pool, slot_ids, k_out=None, v_out=No
 
 
 # ----------------------------------------------------------------------------- prepared calls
+
+def _host_array(a, dtype):
+    """A contiguous host (numpy) copy of a numpy array or torch tensor."""
+    import numpy as np
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a), dtype=dtype)
+
+
+def check_slot_mapping(slot_mapping, num_blocks: int, block_size: int) -> None:
+    """Debug check (host copy): every entry is -1 or a slot of the pool, and no
+    slot is written twice. Raises TQError naming the first offending token
+    (its index also in the exception's `index`)."""
+    import numpy as np
+    m = _host_array(slot_mapping, np.int64).reshape(-1)
+    bad = _i64(-1)
+    st = _lib.tq_check_slot_mapping(m.ctypes.data if m.size else None, m.size, num_blocks, block_size,
+                                    ctypes.byref(bad))
+    if st != TQ_OK:
+        e = TQError(st, last_error())
+        e.index = bad.value
+        raise e
+
+
+def check_block_tables(block_tables, seq_lens, num_blocks: int, block_size: int) -> None:
+    """Debug check (host copies): each sequence's blocks fit its table row and
+    their ids lie in the pool. Raises TQError naming the first offending
+    (sequence, logical block), also in the exception's `seq` and `block`."""
+    import numpy as np
+    t = _host_array(block_tables, np.int32)
+    n = _host_array(seq_lens, np.int32).reshape(-1)
+    if t.ndim != 2 or t.shape[0] != n.size:
+        raise ValueError("block_tables [batch, max_blocks] and seq_lens [batch] required")
+    bs_, bb = ctypes.c_int(-1), ctypes.c_int(-1)
+    st = _lib.tq_check_block_tables(t.ctypes.data if t.size else None, n.size, t.shape[1],
+                                    n.ctypes.data if n.size else None, num_blocks, block_size,
+                                    ctypes.byref(bs_), ctypes.byref(bb))
+    if st != TQ_OK:
+        e = TQError(st, last_error())
+        e.seq, e.block = bs_.value, bb.value
+        raise e
+
 
 class _Prepared:
     """A library call with its arguments marshalled once; calling it issues

@@ -9,8 +9,11 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "tq_internal.h"
 
@@ -355,6 +358,85 @@ TQ_EXPORT tq_status tq_decode_workspace_size(const tq_config *cfg, int batch, in
   if (st != TQ_OK) return st;
   *bytes_out = plan.workspace_bytes;
   if (num_splits_out) *num_splits_out = plan.max_splits + plan.ring_chunks;
+  return TQ_OK;
+}
+
+// Debug checks of caller data in host memory. The kernels clamp or skip bad
+// device-side ids (an out-of-range slot is not written, a token of an
+// out-of-range block is masked) and two tokens mapped to one slot race; these
+// make such inputs visible before a call instead.
+TQ_EXPORT tq_status tq_check_slot_mapping(const int64_t *slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                                          int block_size, int64_t *bad_index) {
+  if (bad_index) *bad_index = -1;
+  if (num_tokens < 0 || num_blocks < 0 || block_size <= 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_check_slot_mapping: need num_tokens >= 0, num_blocks >= 0, block_size > 0");
+  if (num_tokens > 0 && !slot_mapping) return fail(TQ_ERR_INVALID_ARG, "tq_check_slot_mapping: slot_mapping is NULL");
+  if (num_blocks > INT64_MAX / block_size)
+    return fail(TQ_ERR_INVALID_ARG, "tq_check_slot_mapping: num_blocks * block_size overflows");
+  const int64_t cap = num_blocks * block_size;
+  std::vector<std::pair<int64_t, int64_t>> used;  // (slot, token)
+  used.reserve(static_cast<size_t>(num_tokens));
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    const int64_t slot = slot_mapping[i];
+    if (slot == -1) continue;  // skipped token
+    if (slot < 0 || slot >= cap) {
+      if (bad_index) *bad_index = i;
+      return fail(TQ_ERR_INVALID_ARG, "tq_check_slot_mapping: token " + std::to_string(i) + " maps to slot " +
+                                          std::to_string(slot) + ", outside the pool's " + std::to_string(cap) +
+                                          " slots");
+    }
+    used.emplace_back(slot, i);
+  }
+  std::sort(used.begin(), used.end());
+  // the first token (in token order) whose slot an earlier token also takes
+  int64_t worst = -1, slot_of = 0, first_of = 0;
+  for (size_t j = 1; j < used.size(); ++j) {
+    if (used[j].first == used[j - 1].first && (worst < 0 || used[j].second < worst)) {
+      worst = used[j].second;
+      slot_of = used[j].first;
+      first_of = used[j - 1].second;
+    }
+  }
+  if (worst >= 0) {
+    if (bad_index) *bad_index = worst;
+    return fail(TQ_ERR_INVALID_ARG, "tq_check_slot_mapping: tokens " + std::to_string(first_of) + " and " +
+                                        std::to_string(worst) + " both write slot " + std::to_string(slot_of));
+  }
+  clear_error();
+  return TQ_OK;
+}
+
+TQ_EXPORT tq_status tq_check_block_tables(const int32_t *block_tables, int batch, int max_blocks_per_seq,
+                                          const int32_t *seq_lens, int64_t num_blocks, int block_size,
+                                          int *bad_seq, int *bad_block) {
+  if (bad_seq) *bad_seq = -1;
+  if (bad_block) *bad_block = -1;
+  if (batch < 0 || max_blocks_per_seq < 0 || num_blocks < 0 || block_size <= 0)
+    return fail(TQ_ERR_INVALID_ARG,
+                "tq_check_block_tables: need batch >= 0, max_blocks_per_seq >= 0, num_blocks >= 0, block_size > 0");
+  if (batch > 0 && (!seq_lens || (max_blocks_per_seq > 0 && !block_tables)))
+    return fail(TQ_ERR_INVALID_ARG, "tq_check_block_tables: NULL pointer");
+  for (int b = 0; b < batch; ++b) {
+    const int64_t len = seq_lens[b];
+    const int64_t need = (std::max<int64_t>(len, 0) + block_size - 1) / block_size;
+    if (len < 0 || need > max_blocks_per_seq) {
+      if (bad_seq) *bad_seq = b;
+      return fail(TQ_ERR_INVALID_ARG, "tq_check_block_tables: sequence " + std::to_string(b) + " has length " +
+                                          std::to_string(len) + ", which its table row of " +
+                                          std::to_string(max_blocks_per_seq) + " blocks cannot hold");
+    }
+    for (int64_t i = 0; i < need; ++i) {
+      const int32_t id = block_tables[static_cast<int64_t>(b) * max_blocks_per_seq + i];
+      if (id < 0 || id >= num_blocks) {
+        if (bad_seq) *bad_seq = b;
+        if (bad_block) *bad_block = static_cast<int>(i);
+        return fail(TQ_ERR_INVALID_ARG, "tq_check_block_tables: sequence " + std::to_string(b) + ", logical block " +
+                                            std::to_string(i) + " has id " + std::to_string(id) +
+                                            ", outside the pool's " + std::to_string(num_blocks) + " blocks");
+      }
+    }
+  }
+  clear_error();
   return TQ_OK;
 }
 

@@ -396,6 +396,34 @@ tq_status tq_dequant(const tq_config *cfg, int layer_idx,
                      int block_size, const int64_t *slot_ids, int64_t n,
                      float *k_out, float *v_out, void *stream);
 
+/*
+ * Debug checks of caller data, in host memory (no device access, no stream).
+ * The calls above clamp or skip bad device-side ids instead of failing: a
+ * slot outside the pool is not written, a token of a block outside the pool
+ * is masked, and two tokens mapped to one slot race. These checks, run on a
+ * host copy before a call, report such inputs. The block/slot space is the
+ * paged layout above ([PR] page-size snippet: block_size tokens per block;
+ * slot = block * block_size + offset).
+ *
+ * tq_check_slot_mapping: every entry of slot_mapping[num_tokens] is -1 (skip)
+ * or a slot in [0, num_blocks * block_size), and no slot appears twice.
+ * TQ_OK, or TQ_ERR_INVALID_ARG with *bad_index (nullable) = the first
+ * offending token (for a repeated slot: the later of the two tokens) and a
+ * message naming it; *bad_index = -1 on success.
+ *
+ * tq_check_block_tables: for each sequence b, seq_lens[b] >= 0, its
+ * ceil(seq_lens[b] / block_size) logical blocks fit the table row
+ * (max_blocks_per_seq), and each of their ids in block_tables[b][i] lies in
+ * [0, num_blocks). Blocks shared between sequences are allowed. TQ_OK, or
+ * TQ_ERR_INVALID_ARG with *bad_seq / *bad_block (nullable; bad_block -1 when
+ * the length itself is at fault).
+ */
+tq_status tq_check_slot_mapping(const int64_t *slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                                int block_size, int64_t *bad_index);
+tq_status tq_check_block_tables(const int32_t *block_tables, int batch, int max_blocks_per_seq,
+                                const int32_t *seq_lens, int64_t num_blocks, int block_size,
+                                int *bad_seq, int *bad_block);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *tq_last_error(void);
 

@@ -276,3 +276,43 @@ def test_ring_argument_errors_before_launch():
     assert _c_call("tq_ring_append", cfgp, None, al, 2, 8, al, al, 128, al, None) == 1
     assert _c_call("tq_ring_append", cfgp, al, al, 2, 8, al + 4, al, 128, al, None) == 1
     assert _c_call("tq_ring_append", cfgp, None, None, 0, 8, None, None, 128, None, None) == 0
+
+
+def test_check_slot_mapping():
+    """The host debug check of a slot mapping: -1 skips, range, repeats."""
+    tq.check_slot_mapping(np.array([0, 5, -1, 63, -1, 17], np.int64), 4, 16)   # 64 slots
+    tq.check_slot_mapping(np.zeros(0, np.int64), 0, 16)
+    for bad, idx in (([0, 64, 3], 1), ([3, -2], 1), ([7, 8, 9, 8, 7], 3), ([1, 1], 1)):
+        with pytest.raises(tq.TQError) as ei:
+            tq.check_slot_mapping(np.array(bad, np.int64), 4, 16)
+        assert ei.value.status == tq.TQ_ERR_INVALID_ARG and ei.value.index == idx, (bad, ei.value.index)
+    # the message names the two tokens of a repeated slot
+    with pytest.raises(tq.TQError, match="tokens 0 and 3 both write slot 7"):
+        tq.check_slot_mapping(np.array([7, 1, 2, 7], np.int64), 4, 16)
+    # raw C-ABI: argument errors, NULL out-parameter
+    lib = tq.lib()
+    assert lib.tq_check_slot_mapping(None, 3, 4, 16, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_check_slot_mapping(None, 0, 4, 0, None) == tq.TQ_ERR_INVALID_ARG
+    m = np.array([1, 2, 2], np.int64)
+    assert lib.tq_check_slot_mapping(m.ctypes.data, 3, 4, 16, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_check_slot_mapping(m.ctypes.data, 2, 4, 16, None) == tq.TQ_OK
+
+
+def test_check_block_tables():
+    """The host debug check of block tables against lengths and the pool."""
+    tables = np.array([[3, 0, 9], [1, -1, -1]], np.int32)
+    tq.check_block_tables(tables, np.array([40, 16], np.int32), 10, 16)     # 3 and 1 blocks used
+    tq.check_block_tables(tables, np.array([0, 0], np.int32), 10, 16)
+    cases = [
+        (np.array([[3, 0, 10], [1, 0, 0]], np.int32), [40, 16], (0, 2)),   # id past the pool
+        (np.array([[3, 0, 9], [1, -1, 0]], np.int32), [40, 17], (1, 1)),   # negative id in use
+        (tables, [49, 16], (0, -1)),                                       # 4 blocks, row of 3
+        (tables, [40, -1], (1, -1)),                                       # negative length
+    ]
+    for t, lens, where in cases:
+        with pytest.raises(tq.TQError) as ei:
+            tq.check_block_tables(t, np.array(lens, np.int32), 10, 16)
+        assert ei.value.status == tq.TQ_ERR_INVALID_ARG and (ei.value.seq, ei.value.block) == where, (lens, where)
+    lib = tq.lib()
+    assert lib.tq_check_block_tables(None, 1, 3, None, 10, 16, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_check_block_tables(None, 0, 3, None, 10, 16, None, None) == tq.TQ_OK
