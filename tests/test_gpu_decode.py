@@ -83,7 +83,7 @@ SCEN = {
     "d64_k3v4": (64, 3, 4, False, 4, 2, [512], None, 0),
     "d96_k8v3": (96, 8, 3, False, 12, 4, [257, 64], None, 0),
     "d64_k4v3_ring": (64, 4, 3, True, 6, 2, [95, 40], [17, 128], 128),
-    # ring capacity not a multiple of the 64-token ring chunk; a full chunk,
+    # ring capacity not a multiple of the 32-token ring chunk; full chunks,
     # a partial second chunk and a ring-only sequence
     "d96_k3v4_ring100": (96, 3, 4, True, 16, 4, [50, 300, 0], [100, 70, 64], 100),
     # 2-bit values at each column packing (G = 4, 8, 16 query heads per KV head)
