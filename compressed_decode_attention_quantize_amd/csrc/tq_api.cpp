@@ -59,7 +59,8 @@ TQ_EXPORT tq_status tq_quantize_append(const tq_config *cfg, int layer_idx, cons
   p.slot_bytes = cfg->slot_size_aligned;
   p.key_bytes = cfg->key_packed_size;
   layer_sign_mask(*cfg, layer_idx, p.sign_words);
-  for (int i = 0; i < 15; ++i) p.midpoints[i] = cfg->midpoints[i];
+  if (!cfg->key_fp8 && !lloyd_max_bins(*cfg, p))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_quantize_append: the config's midpoints do not fit the index bins");
   p.sqrt_block = static_cast<float>(std::sqrt(static_cast<double>(cfg->wht_block)));
   const int err = launch_quantize(*cfg, in_dtype, p, stream);
   if (err != hipSuccess) return hip_fail("tq_quantize_append launch", err);
@@ -93,7 +94,8 @@ TQ_EXPORT tq_status tq_ring_flush(const tq_config *cfg, int layer_idx, const uin
   p.slot_bytes = cfg->slot_size_aligned;
   p.key_bytes = cfg->key_packed_size;
   layer_sign_mask(*cfg, layer_idx, p.sign_words);
-  for (int i = 0; i < 15; ++i) p.midpoints[i] = cfg->midpoints[i];
+  if (!cfg->key_fp8 && !lloyd_max_bins(*cfg, p))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_ring_flush: the config's midpoints do not fit the index bins");
   p.sqrt_block = static_cast<float>(std::sqrt(static_cast<double>(cfg->wht_block)));
   p.ring_lens = ring_lens;
   p.seq_lens = seq_lens;

@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <limits>
 #include <string>
 #include <utility>
 #include <vector>
@@ -137,6 +138,51 @@ tq_status check_config(const tq_config *cfg) {
     return fail(TQ_ERR_INVALID_ARG, "config was modified after tq_config_init");
   clear_error();
   return TQ_OK;
+}
+
+namespace {
+
+// The bin of x exactly as the quantize kernel computes it: one correctly
+// rounded fma, a clamp to [0, kLmBins - 1] (a NaN becomes 0), truncation.
+// Every step is non-decreasing in x.
+int lm_bin(float x, float scale, float offset) {
+  const float t = std::fmin(std::fmax(std::fma(x, scale, offset), 0.0f), static_cast<float>(kLmBins - 1));
+  return static_cast<int>(t);
+}
+
+}  // namespace
+
+// The Lloyd-Max index of u is the number of midpoints strictly below u
+// (vLLM API page, TurboQuantConfig: Lloyd-Max keys). With bin() non-decreasing
+// and at most one midpoint per bin, every midpoint in a bin below bin(u) is
+// below u and every one in a bin above is above it, so the count is the
+// number of midpoints in lower bins plus (u > the midpoint in u's own bin).
+// A NaN u falls in bin 0, below every midpoint's bin, and gets 0.
+bool lloyd_max_bins(const tq_config &cfg, QuantParams &p) {
+  const int nm = cfg.n_centroids - 1;
+  if (nm < 1 || nm > 15) return false;
+  const double lo = cfg.midpoints[0], hi = cfg.midpoints[nm - 1];
+  if (!std::isfinite(lo) || !std::isfinite(hi) || !(hi > lo)) return false;
+  const double w = (hi - lo) / (kLmBins - 2);
+  p.lm_scale = static_cast<float>(1.0 / w);
+  p.lm_offset = static_cast<float>(1.0 - lo / w);
+  int bins[15];
+  for (int k = 0; k < nm; ++k) {
+    bins[k] = lm_bin(cfg.midpoints[k], p.lm_scale, p.lm_offset);
+    if (k > 0 && bins[k] <= bins[k - 1]) return false;
+  }
+  const float inf = std::numeric_limits<float>::infinity();
+  for (int j = 0; j < kLmBins; ++j) {
+    float mid = inf;
+    uint32_t below = 0;
+    for (int k = 0; k < nm; ++k) {
+      if (bins[k] < j) ++below;
+      if (bins[k] == j) mid = cfg.midpoints[k];
+    }
+    std::memcpy(&p.lm_table[2 * j], &mid, sizeof(mid));
+    p.lm_table[2 * j + 1] = below;
+  }
+  return true;
 }
 
 void layer_sign_mask(const tq_config &cfg, int layer_idx, uint32_t words[4]) {

@@ -19,9 +19,20 @@ void clear_error();
 // Validates a config filled by tq_config_init (recomputes the derived sizes).
 tq_status check_config(const tq_config *cfg);
 
+struct QuantParams;
+// Fills the Lloyd-Max bin fields of p from the config's midpoints: kLmBins
+// equal bins, the first midpoint in bin 1 and the last in bin kLmBins - 1.
+// Returns false when two midpoints fall in one bin (or are out of order),
+// where the table cannot give the exact count.
+bool lloyd_max_bins(const tq_config &cfg, QuantParams &p);
+
 // Random signs of one layer as a bit mask: bit j of words[j / 32] is set when
 // sign j is -1. head_dim <= 128.
 void layer_sign_mask(const tq_config &cfg, int layer_idx, uint32_t words[4]);
+
+// Bins of the Lloyd-Max index table (a power of two; at most one midpoint
+// falls in each bin for every table tq_config_init makes).
+constexpr int kLmBins = 64;
 
 // Kernel parameter blocks. Plain structs passed by value to the kernels.
 struct QuantParams {
@@ -38,8 +49,13 @@ struct QuantParams {
   int32_t slot_bytes;   // slot_size_aligned
   int32_t key_bytes;    // key_packed_size
   uint32_t sign_words[4];
-  float midpoints[15];
   float sqrt_block;     // fp32(sqrt(B))
+  // Lloyd-Max index by bins (MSE keys; see lloyd_max_bins): bin(u) =
+  // trunc(min(max(fma(u, lm_scale, lm_offset), 0), kLmBins - 1)), entry j =
+  // {bits of the midpoint in bin j (+inf if none), midpoints in bins < j}.
+  float lm_scale;
+  float lm_offset;
+  uint32_t lm_table[2 * kLmBins];
   // Ring flush mode (ring_lens != nullptr): token n is ring position
   // n % ring_cap of sequence n / ring_cap, read at
   // (seq * num_kv_heads + h) * ring_cap * D + pos * D; it is written only if

@@ -60,42 +60,25 @@ __device__ __forceinline__ uint32_t load_group(const uint8_t *field, int r) {
   return w;
 }
 
-// Lloyd-Max index of u: the number of the 2^KB - 1 ascending midpoints that
-// lie strictly below u. A branch-free binary search: each level compares u
-// with the midpoint that the earlier answers select, so KB compares replace
-// the 2^KB - 1 of a linear count, with the same result for every u (a NaN
-// compares false everywhere and gets 0, as the count gives). The midpoints
-// come as separate register values: selecting between array elements would
-// become a load from a selected address.
-__device__ __forceinline__ uint32_t lm_index3(float u, float m0, float m1, float m2, float m3, float m4, float m5,
-                                              float m6) {
-  const bool b2 = u > m3;
-  const bool b1 = u > (b2 ? m5 : m1);
-  float q0 = b1 ? m2 : m0, q1 = b1 ? m6 : m4;
-  asm("" : "+v"(q0), "+v"(q1));  // both candidates, then one select (no branch)
-  const bool b0 = u > (b2 ? q1 : q0);
-  return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
-}
-__device__ __forceinline__ uint32_t lm_index4(float u, float m0, float m1, float m2, float m3, float m4, float m5,
-                                              float m6, float m7, float m8, float m9, float m10, float m11,
-                                              float m12, float m13, float m14) {
-  const bool b3 = u > m7;
-  const bool b2 = u > (b3 ? m11 : m3);
-  float r0 = b2 ? m5 : m1, r1 = b2 ? m13 : m9;
-  asm("" : "+v"(r0), "+v"(r1));  // all candidates, then selects (no branch)
-  const bool b1 = u > (b3 ? r1 : r0);
-  float q0 = b1 ? m2 : m0, q1 = b1 ? m6 : m4;
-  float q2 = b1 ? m10 : m8, q3 = b1 ? m14 : m12;
-  asm("" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3));
-  float s0 = b2 ? q1 : q0, s1 = b2 ? q3 : q2;
-  asm("" : "+v"(s0), "+v"(s1));
-  const bool b0 = u > (b3 ? s1 : s0);
-  return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+// Lloyd-Max index of u: the number of midpoints strictly below u, from the
+// bin table the host built (QuantParams::lm_table). bin(u) is the host's bin
+// function step for step (fma, clamp with NaN -> 0, truncation); the table
+// entry holds the bin's midpoint (+inf if none) and the count of midpoints in
+// lower bins, so one compare finishes the count. NaN gets 0.
+__device__ __forceinline__ uint32_t lm_index(float u, float scale, float offset, const uint2 *lut) {
+  const float t = fminf(fmaxf(fmaf(u, scale, offset), 0.0f), static_cast<float>(kLmBins - 1));
+  const uint2 e = lut[static_cast<int>(t)];
+  return e.y + (u > __uint_as_float(e.x) ? 1u : 0u);
 }
 
 template <int D, int KB, int VB, int DT>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   using T = Team<D>;
+  // Lloyd-Max bin table (MSE keys), read before the barrier in the key path
+  __shared__ uint2 lut[KB == 8 ? 1 : kLmBins];
+  if constexpr (KB != 8) {
+    if (threadIdx.x < kLmBins) lut[threadIdx.x] = make_uint2(p.lm_table[2 * threadIdx.x], p.lm_table[2 * threadIdx.x + 1]);
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int team = lane / T::kLanes;
@@ -173,24 +156,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     const float pn = n * p.sqrt_block;
     const float rcp = (n == 0.0f) ? 0.0f : 1.0f / pn;
     static_assert(KB == 3 || KB == 4, "MSE key widths");
-    // the midpoints in VGPRs once per lane (a select takes one scalar operand)
-    float md[(1 << KB) - 1];
-#pragma unroll
-    for (int k = 0; k < (1 << KB) - 1; ++k) {
-      md[k] = p.midpoints[k];
-      asm("" : "+v"(md[k]));
-    }
+    __syncthreads();  // the bin table is in LDS (no thread has left the kernel)
     uint32_t idx[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float u = z[i] * rcp;
-      if constexpr (KB == 3) {
-        idx[i] = lm_index3(u, md[0], md[1], md[2], md[3], md[4], md[5], md[6]);
-      } else {
-        idx[i] = lm_index4(u, md[0], md[1], md[2], md[3], md[4], md[5], md[6], md[7], md[8], md[9], md[10], md[11],
-                           md[12], md[13], md[14]);
-      }
-    }
+    for (int i = 0; i < 8; ++i) idx[i] = lm_index(z[i] * rcp, p.lm_scale, p.lm_offset, lut);
     const uint32_t w = pack8<KB>(idx);
     if (write) {
       store_field<KB>(dst + KB * r, w);
