@@ -59,30 +59,7 @@ __device__ __forceinline__ float e4m3fn_to_float(uint32_t c) {
 }
 
 // ---------------------------------------------------------------------------
-// loads of 8 consecutive elements as fp32 (16-byte aligned source)
-
-template <int DT>  // 0 = f32, 1 = bf16, 2 = f16 (tq_dtype values)
-__device__ __forceinline__ void load8(const void *base, int64_t elem, float x[8]) {
-  if constexpr (DT == 0) {
-    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem);
-    const float4 a = p[0], b = p[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  } else {
-    const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (DT == 1) {
-        x[2 * i] = bf16_bits_to_float(w[i] & 0xffffu);
-        x[2 * i + 1] = bf16_bits_to_float(w[i] >> 16);
-      } else {
-        x[2 * i] = f16_bits_to_float(w[i] & 0xffffu);
-        x[2 * i + 1] = f16_bits_to_float(w[i] >> 16);
-      }
-    }
-  }
-}
+// element loads as fp32
 
 __device__ __forceinline__ float load_as_float(const void *base, int dtype, int64_t i) {
   if (dtype == 0) return static_cast<const float *>(base)[i];

@@ -36,6 +36,47 @@ __device__ __forceinline__ void store_field(uint8_t *dst, uint32_t w) {
   }
 }
 
+// The 8 consecutive elements of a lane, read as raw bits (16-byte aligned
+// source): one 16-byte load for bf16/f16 (a), two for f32 (a, b).
+template <int DT>  // 0 = f32, 1 = bf16, 2 = f16 (tq_dtype values)
+__device__ __forceinline__ void load_raw8(const void *base, int64_t elem, uint4 &a, uint4 &b) {
+  if constexpr (DT == 0) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
+    a = q[0];
+    b = q[1];
+  } else {
+    a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
+  }
+}
+
+// Raw bits of load_raw8 as fp32 (exact for every input format).
+template <int DT>
+__device__ __forceinline__ void widen8(const uint4 &a, const uint4 &b, float x[8]) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  if constexpr (DT == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == 1) {
+        x[2 * i] = bf16_bits_to_float(w[i] & 0xffffu);
+        x[2 * i + 1] = bf16_bits_to_float(w[i] >> 16);
+      } else {
+        x[2 * i] = f16_bits_to_float(w[i] & 0xffffu);
+        x[2 * i + 1] = f16_bits_to_float(w[i] >> 16);
+      }
+    }
+  }
+}
+
+// The 8 sign bits of lane r (bit i: element 8r + i is negated) from the four
+// mask words held as values, so no lane reads a word from a selected address.
+__device__ __forceinline__ uint32_t lane_signs(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, int r) {
+  const uint32_t word = r < 8 ? (r < 4 ? w0 : w1) : (r < 12 ? w2 : w3);
+  return (word >> (8 * (r & 3))) & 0xffu;
+}
+
 template <int BITS>
 __device__ __forceinline__ uint32_t pack8(const uint32_t c[8]) {
   uint32_t w = 0;
@@ -74,11 +115,6 @@ __device__ __forceinline__ uint32_t lm_index(float u, float scale, float offset,
 template <int D, int KB, int VB, int DT>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   using T = Team<D>;
-  // Lloyd-Max bin table (MSE keys), read before the barrier in the key path
-  __shared__ uint2 lut[KB == 8 ? 1 : kLmBins];
-  if constexpr (KB != 8) {
-    if (threadIdx.x < kLmBins) lut[threadIdx.x] = make_uint2(p.lm_table[2 * threadIdx.x], p.lm_table[2 * threadIdx.x + 1]);
-  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int team = lane / T::kLanes;
@@ -92,12 +128,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   const int64_t t = active ? tok : 0;
   const int h = static_cast<int>(blockIdx.y);
 
-  // source element offsets of this (token, head) row, and its slot
-  int64_t k_off, v_off, slot = -1;
+  // the row bits of this (token, head), and its slot; zeros where nothing is
+  // read (the team then computes on zeros and writes nothing)
+  int64_t slot = -1;
+  uint4 xa = make_uint4(0, 0, 0, 0), xb = xa, va = xa, vb = xa;
   if (p.ring_lens) {
+    // ring flush: token t is position pos of sequence seq; a ring that is not
+    // full is not read. A team shares its token, so this is uniform per team.
     const int64_t seq = t / p.ring_cap;
     const int pos = static_cast<int>(t - seq * p.ring_cap);
-    k_off = v_off = ((seq * p.num_kv_heads + h) * p.ring_cap + pos) * D;
     if (active && p.ring_lens[seq] >= p.ring_cap) {
       const int64_t at = static_cast<int64_t>(max(p.seq_lens[seq], 0)) + pos;
       const int64_t lblk = at / p.block_size;
@@ -106,21 +145,26 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
         if (phys >= 0) slot = phys * p.block_size + (at - lblk * p.block_size);
       }
     }
-  } else {
-    k_off = t * p.k_stride + static_cast<int64_t>(h) * D;
-    v_off = t * p.v_stride + static_cast<int64_t>(h) * D;
-    if (active) slot = p.slot_mapping[t];
+    if (slot >= 0) {
+      const int64_t off = ((seq * p.num_kv_heads + h) * p.ring_cap + pos) * D + 8 * r;
+      load_raw8<DT>(p.k, off, xa, xb);
+      load_raw8<DT>(p.v, off, va, vb);
+    }
+  } else if (active) {
+    // the slot id and both rows are independent reads, issued together
+    slot = p.slot_mapping[t];
+    load_raw8<DT>(p.k, t * p.k_stride + static_cast<int64_t>(h) * D + 8 * r, xa, xb);
+    load_raw8<DT>(p.v, t * p.v_stride + static_cast<int64_t>(h) * D + 8 * r, va, vb);
+  }
+  // Lloyd-Max bin table (MSE keys) into LDS, behind the row reads; read after
+  // the barrier in the key path
+  __shared__ uint2 lut[KB == 8 ? 1 : kLmBins];
+  if constexpr (KB != 8) {
+    if (threadIdx.x < kLmBins) lut[threadIdx.x] = make_uint2(p.lm_table[2 * threadIdx.x], p.lm_table[2 * threadIdx.x + 1]);
   }
   float x[8], v[8];
-  // a ring that is not full is not read (its team computes on zeros and
-  // writes nothing); a team shares its token, so this is uniform per team
-  if (active && (p.ring_lens == nullptr || slot >= 0)) {
-    load8<DT>(p.k, k_off + 8 * r, x);
-    load8<DT>(p.v, v_off + 8 * r, v);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = v[i] = 0.0f;
-  }
+  widen8<DT>(xa, xb, x);
+  widen8<DT>(va, vb, v);
   const bool write = active && slot >= 0 && slot < p.total_slots;
   if (!write) slot = 0;
   int64_t blk, off;
@@ -148,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   } else {
     const float n2 = team_sumsq<D>(x, team_base);
     const float n = sqrtf(n2);
-    const uint32_t sbits = lane_sign_bits(p.sign_words, r);
+    const uint32_t sbits = lane_signs(p.sign_words[0], p.sign_words[1], p.sign_words[2], p.sign_words[3], r);
     float z[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) z[i] = flip_sign(x[i], (sbits >> i) & 1u);
