@@ -198,13 +198,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     for (int i = 0; i < 8; ++i) z[i] = flip_sign(x[i], (sbits >> i) & 1u);
     team_wht<D>(z, lane_in_block);
     const float pn = n * p.sqrt_block;
-    const float rcp = (n == 0.0f) ? 0.0f : 1.0f / pn;
+    // divide unconditionally and select (no branch between the WHT's lane
+    // moves and their adds)
+    const float inv_pn = 1.0f / pn;
+    const float rcp = (n == 0.0f) ? 0.0f : inv_pn;
     static_assert(KB == 3 || KB == 4, "MSE key widths");
     __syncthreads();  // the bin table is in LDS (no thread has left the kernel)
     uint32_t idx[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) idx[i] = lm_index(z[i] * rcp, p.lm_scale, p.lm_offset, lut);
-    const uint32_t w = pack8<KB>(idx);
+    uint32_t w = pack8<KB>(idx);
+    // computed before the store branch, so the WHT's last lane moves stay in
+    // one block with their adds (and fold into them)
+    asm volatile("" : "+v"(w));
     if (write) {
       store_field<KB>(dst + KB * r, w);
       if (r == 0) store_field<2>(dst + (D * KB) / 8, float_to_f16_bits(n));

@@ -74,6 +74,35 @@ def test_pool_bytes_bit_exact(d, kb, vb, nc, dtype):
     assert mism.size == 0, f"{len(mism)} bytes differ; first at {mism[:5].tolist()}"
 
 
+@pytest.mark.parametrize("d,kb", [(128, 4), (128, 3), (96, 4), (96, 3), (64, 4), (64, 3)])
+def test_keys_on_midpoint_ties_bit_exact(d, kb):
+    """Keys whose rotated coordinates fall exactly on each Lloyd-Max midpoint
+    and one ulp either side (fp32 inputs, so the kernel sees the same
+    coordinates): pool bytes equal the oracle's, and the codes at the tied
+    coordinates are the number of midpoints strictly below."""
+    from tests.midpoint_keys import tie_keys
+    announce(f"quantize midpoint ties d={d} kb={kb}")
+    cfg = tq.config_init(d, kb, 4, False, 42)
+    ocfg = oracle_cfg(cfg)
+    keys, cases = tie_keys(ocfg, layer_idx=2, seed=d + kb)
+    n, bs = len(keys), 16
+    nb = (n + bs - 1) // bs
+    rng = np.random.default_rng(d * 10 + kb)
+    k = keys[:, None, :].copy()
+    v = rng.standard_normal((n, 1, d)).astype(np.float32)
+    mapping = np.arange(n, dtype=np.int64)
+    pool = torch.zeros((nb, 1, bs, cfg.slot_size_aligned), dtype=torch.uint8, device="cuda")
+    tq.quantize_append(cfg, 2, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                       torch.from_numpy(mapping).cuda(), pool)
+    got = pool.cpu().numpy()
+    want = oracle_pool(ocfg, 2, k, v, mapping, nb, 1, bs)
+    mism = np.argwhere(got != want)
+    assert mism.size == 0, f"{len(mism)} bytes differ; first at {mism[:5].tolist()}"
+    idx = OX.decode_slot_fields(got.reshape(-1, cfg.slot_size_aligned)[:n], ocfg)["idx"]
+    for row, i, kk, off in cases:
+        assert idx[row, i] == (kk + 1 if off > 0 else kk), (row, i, kk, off)
+
+
 def test_tiny_workload_prefill_then_decode_append():
     """511 tokens appended in bulk, then one more (the tiny workload)."""
     from workloads import tiny_numpy

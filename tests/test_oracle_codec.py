@@ -158,6 +158,37 @@ def test_key_distortion_matches_lloyd_max_theory(kb, expect):
     assert abs(rel.mean() - expect) / expect < 0.1
 
 
+@pytest.mark.parametrize("d,kb", [(128, 4), (128, 3), (96, 4), (96, 3), (64, 4), (64, 3)])
+def test_key_index_at_midpoint_ties(d, kb):
+    """Rotated coordinates exactly on each midpoint m_k, and one fp32 ulp
+    above and below it: the index is the number of midpoints strictly below
+    u (k on the midpoint, k + 1 above, k below). A >= in place of the strict
+    compare, or an off-by-one bin, fails here."""
+    from tests.midpoint_keys import rotated_unit, tie_keys
+    cfg = _cfg(d, kb)
+    keys, cases = tie_keys(cfg, layer_idx=1, seed=d + kb)
+    _, m32 = LM.tables_f32(d, kb)
+    u = rotated_unit(keys, cfg, 1)
+    idx, _ = X.encode_keys_mse(keys, cfg, 1)
+    # u in float64 straight from the definition, to check the keys' u
+    blk = cfg.wht_block
+    s = R.signs(42, 1, d).astype(np.float64)
+    h = scipy.linalg.block_diag(*([scipy.linalg.hadamard(blk)] * (d // blk))).astype(np.float64)
+    x64 = keys.astype(np.float64)
+    u64 = (x64 * s) @ h.T / (math.sqrt(blk) * np.linalg.norm(x64, axis=1, keepdims=True))
+    seen = set()
+    for row, i, k, off in cases:
+        m = m32[k]
+        target = m if off == 0 else np.nextafter(m, np.float32(np.inf if off > 0 else -np.inf))
+        assert u[row, i] == target
+        assert abs(u64[row, i] - float(target)) <= 1e-5 * max(abs(float(m)), 1e-3)
+        assert idx[row, i] == (k + 1 if off > 0 else k), (row, i, k, off)
+        seen.add((k, off))
+    # every midpoint is tied from both sides (the zero midpoint only exactly)
+    nz = [k for k in range(len(m32)) if m32[k] != 0]
+    assert seen == {(k, o) for k in nz for o in (-1, 0, 1)} | {(k, 0) for k in range(len(m32)) if m32[k] == 0}
+
+
 def test_zero_key_vector():
     cfg = _cfg(128, 3)
     x = np.zeros((2, 128), np.float32)
