@@ -185,6 +185,10 @@ tq_status tq_layer_signs(const tq_config *cfg, int layer_idx, float *signs_out);
  *  kv_pool       device uint8, layout in the header comment, 16-byte aligned.
  *  num_kv_heads  at most 65535 (TQ_ERR_UNSUPPORTED otherwise; also for
  *                tq_ring_flush).
+ * The index count is read from a table of equal bins over the midpoints with
+ * at most one midpoint per bin; a config whose midpoints do not allow that
+ * (never one tq_config_init made) gets TQ_ERR_UNSUPPORTED, here and in
+ * tq_ring_flush.
  *
  * Keys (MSE mode): vec_norm = fp16(||k||), u = Pi k / ||k|| with
  * Pi = (1/sqrt(B)) H_B diag(signs), index j = number of midpoints strictly

@@ -156,6 +156,24 @@ def test_quantize_argument_errors_before_launch():
     assert _c_call("tq_quantize_append", ctypes.byref(bad), 0, al, al, 1, 4, 8, 1024, 1024, al, al, 10, 16, None) == 1
 
 
+@pytest.mark.parametrize("preset,d", [("turboquant_4bit_nc", 128), ("turboquant_3bit_nc", 96), ("turboquant_k3v4_nc", 64)])
+def test_midpoints_that_share_an_index_bin_are_refused(preset, d):
+    """The Lloyd-Max index is read from equal bins holding at most one
+    midpoint each: two midpoints edited to within a bin of each other make
+    both append entry points refuse the config before any launch."""
+    buf = ctypes.create_string_buffer(4096 + 16)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    c = tq.config_from_preset(preset, d)
+    nm = c.n_centroids - 1
+    span = c.midpoints[nm - 1] - c.midpoints[0]
+    k = nm // 2
+    c.midpoints[k + 1] = c.midpoints[k] + span / 1000.0
+    assert _c_call("tq_quantize_append", ctypes.byref(c), 0, al, al, 1, 4, 8, 1024, 1024, al, al, 10, 16, None) == 3
+    assert "bins" in tq.last_error()
+    assert _c_call("tq_ring_flush", ctypes.byref(c), 0, al, al, 128, al, al, al, 4, 2, 8, al, 10, 16, None) == 3
+    assert "bins" in tq.last_error()
+
+
 def _decode(c, **kw):
     buf = ctypes.create_string_buffer(1 << 16)
     al = (ctypes.addressof(buf) + 15) & ~15
