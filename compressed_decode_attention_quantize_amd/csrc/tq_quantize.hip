@@ -77,6 +77,49 @@ __device__ __forceinline__ uint32_t lane_signs(uint32_t w0, uint32_t w1, uint32_
   return (word >> (8 * (r & 3))) & 0xffu;
 }
 
+// Minimum (or maximum) over a 16- or 8-lane row block of values that are
+// already canonical (outputs of arithmetic: no signalling NaN), with the DPP
+// lane moves folded into v_min/v_max. The compiler's fminf/fmaxf re-quiet a
+// DPP-moved operand first, as it cannot tell it is canonical; for canonical
+// operands IEEE-mode v_min/v_max give exactly fminf/fmaxf (a quiet NaN loses
+// to a number). Each step opens with two wait states: a DPP source must not
+// be read right after a VALU op writes it.
+template <int LANES, bool MAX>
+__device__ __forceinline__ float row_reduce_canonical(float v) {
+  static_assert(LANES == 8 || LANES == 16, "row block");
+  float t, u;
+  if constexpr (MAX) {
+    asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                 : "=&v"(t) : "v"(v));
+    asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                 : "=&v"(u) : "v"(t));
+    asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                 : "=&v"(t) : "v"(u));
+    asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %2 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                 : "=&v"(v) : "v"(t), "v"(u));
+    if constexpr (LANES == 16)
+      asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                   : "=&v"(t) : "v"(v));
+    else
+      t = v;
+  } else {
+    asm volatile("s_nop 1\n\tv_min_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                 : "=&v"(t) : "v"(v));
+    asm volatile("s_nop 1\n\tv_min_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                 : "=&v"(u) : "v"(t));
+    asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                 : "=&v"(t) : "v"(u));
+    asm volatile("s_nop 1\n\tv_min_f32_dpp %0, %1, %2 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                 : "=&v"(v) : "v"(t), "v"(u));
+    if constexpr (LANES == 16)
+      asm volatile("s_nop 1\n\tv_min_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                   : "=&v"(t) : "v"(v));
+    else
+      t = v;
+  }
+  return t;
+}
+
 template <int BITS>
 __device__ __forceinline__ uint32_t pack8(const uint32_t c[8]) {
   uint32_t w = 0;
@@ -218,14 +261,25 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   }
 
   // ---- values
+  // quieted first: a signalling NaN is then skipped by min and max like any
+  // NaN (v_min3/v_max3 would return it), and the lane reductions below see
+  // canonical values only
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __builtin_canonicalizef(v[i]);
   float mn = v[0], mx = v[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) {
     mn = fminf(mn, v[i]);
     mx = fmaxf(mx, v[i]);
   }
-  mn = team_min<D>(mn, team_base);
-  mx = team_max<D>(mx, team_base);
+  if constexpr (T::kBlocks == 1) {
+    // one row block per vector (D = 64, 128); in-lane results are canonical
+    mn = row_reduce_canonical<T::kBlockLanes, false>(mn);
+    mx = row_reduce_canonical<T::kBlockLanes, true>(mx);
+  } else {
+    mn = team_min<D>(mn, team_base);
+    mx = team_max<D>(mx, team_base);
+  }
   constexpr float kLevels = static_cast<float>((1 << VB) - 1);
   const float scale32 = (mx - mn) / kLevels;
   const uint32_t s16 = float_to_f16_bits(scale32);

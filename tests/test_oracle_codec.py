@@ -247,9 +247,9 @@ def test_non_finite_keys_hand_worked_bytes():
 def test_non_finite_values_hand_worked_bytes():
     """Values holding a NaN or an infinity, bytes worked out by hand.
 
-    min and max skip a NaN element, so the integer ramp 0..15 with one NaN
-    keeps scale 1 and zero 0 (fp16 0x3c00, 0x0000), and the NaN element takes
-    code 0. An infinity makes the scale infinite (0x7c00) and 1/scale' = 0, so
+    min and max skip a NaN element, quiet or signalling, so the integer ramp
+    0..15 with one NaN keeps scale 1 and zero 0 (fp16 0x3c00, 0x0000), and the
+    NaN element takes code 0. An infinity makes the scale infinite (0x7c00) and 1/scale' = 0, so
     every code is 0 (finite elements: rint(+-0); the infinite one: inf * 0 =
     NaN -> 0); -inf is also the zero point (0xfc00).
     """
@@ -260,6 +260,10 @@ def test_non_finite_values_hand_worked_bytes():
     v[5] = np.nan
     # codes 0..15 pack as 10 32 54 76 98 ba dc fe; code 5 -> 0 makes byte 2 0x04
     want = "1032047698badcfe" + "1032547698badcfe" * 3 + "003c" + "0000"
+    assert _slot_hex(k, v, 64, 3, 4)[off:off + 36].tobytes().hex() == want
+    # a signalling NaN (quiet bit clear) is skipped the same way
+    v = ramp.copy()
+    v.view(np.uint32)[5] = 0x7F800001
     assert _slot_hex(k, v, 64, 3, 4)[off:off + 36].tobytes().hex() == want
     v = ramp.copy()
     v[1] = np.inf
