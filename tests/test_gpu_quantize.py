@@ -42,6 +42,10 @@ def _inputs(n, hkv, d, seed, dtype):
     v.view(np.uint32)[17, :, 4] = 0x7F800001
     tk = torch.from_numpy(k).to(DT[dtype])
     tv = torch.from_numpy(v).to(DT[dtype])
+    if dtype != "f32":
+        # the 16-bit formats' own signalling-NaN pattern (the conversion above
+        # quiets the f32 one)
+        tv.view(torch.int16)[17, :, 4] = 0x7F81 if dtype == "bf16" else 0x7C01
     return tk, tv, tk.float().numpy(), tv.float().numpy()
 
 
