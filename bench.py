@@ -648,7 +648,8 @@ def main():
                                "quantize_step; event records included)",
                    "instrumented_ms_per_step": instr_ms_step},
         "quantize_bulk": {"tokens": nq, "ms": qms, "tokens_per_s": nq / (qms / 1e3),
-                          "GBps": nq * qbpt / (qms / 1e3) / 1e9, "bytes_per_token": qbpt},
+                          "GBps": nq * qbpt / (qms / 1e3) / 1e9, "bytes_per_token": qbpt,
+                          "frac_hbm_peak": nq * qbpt / (qms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "kernel": "tq_decode_attention (split + reduce kernels)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
