@@ -40,12 +40,14 @@ def _inputs(n, hkv, d, seed, dtype):
     # a signalling NaN (f32 inputs keep its bits): min/max skip it like a
     # quiet NaN, and its code is 0
     v.view(np.uint32)[17, :, 4] = 0x7F800001
+    k.view(np.uint32)[18, :, 6] = 0x7F800001   # and in a key row (MSE: like a NaN; FP8: NaN code)
     tk = torch.from_numpy(k).to(DT[dtype])
     tv = torch.from_numpy(v).to(DT[dtype])
     if dtype != "f32":
         # the 16-bit formats' own signalling-NaN pattern (the conversion above
         # quiets the f32 one)
         tv.view(torch.int16)[17, :, 4] = 0x7F81 if dtype == "bf16" else 0x7C01
+        tk.view(torch.int16)[18, :, 6] = 0x7F81 if dtype == "bf16" else 0x7C01
     return tk, tv, tk.float().numpy(), tv.float().numpy()
 
 
